@@ -1,0 +1,71 @@
+"""Plant plausible mistakes in copies of the oracle; some pin must catch each.
+
+CPU only.  Each case copies oracle/ into a temporary package, applies one
+text substitution (a dropped term, a wrong sign, a wrong index or map, an
+off-by-one mask), imports the copy under a fresh name and runs every pin in
+tests/oracle_pins.py against it.  The case passes when at least one pin fails.
+"""
+
+import importlib.util
+import os
+import shutil
+import sys
+
+import pytest
+
+import oracle_pins
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+MUTATIONS = [
+    ("ring.py", "o = o * c[:, None] + p @ v", "o = o + p @ v", "drop rescale of o"),
+    ("ring.py", "l = l * c + p.sum(axis=1)", "l = l + p.sum(axis=1)", "drop rescale of l"),
+    ("ring.py", "np.exp(m - m_ref)", "np.exp(m_ref - m)", "wrong sign of rescale"),
+    ("ring.py", "m_new = np.maximum(m, s.max(axis=1))", "m_new = s.max(axis=1)", "forget running max"),
+    ("ring.py", "[(p - s) % N for s", "[(p + s) % N for s", "rotation direction"),
+    ("ring.py", "lse = np.where(pos, m + np.log(safe_l)", "lse = np.where(pos, m - np.log(safe_l)", "lse sign"),
+    ("ring.py", "vis = (kp[None, :] <= qp[:, None])", "vis = (kp[None, :] < qp[:, None])", "ring mask excludes diagonal"),
+    ("ring.py", "g = h // G", "g = h % Hkv", "ring GQA head map"),
+    ("ring.py", "out = np.where(pos[:, None], o / safe_l[:, None], 0.0)",
+     "out = np.where(pos[:, None], o, 0.0)", "finalize skips division"),
+    ("attention.py", "vis = (kp[None, :] <= qp[r0:r1, None])", "vis = (kp[None, :] < qp[r0:r1, None])",
+     "full mask excludes diagonal"),
+    ("attention.py", "scale = 1.0 / np.sqrt(D)\n    qp", "scale = 1.0 / D\n    qp", "wrong default scale"),
+    ("attention.py", "g = h // G\n            for r0", "g = h % Hkv\n            for r0", "full GQA head map"),
+    ("attention.py", "s = (q_rows @ k.T) * scale", "s = (q_rows @ k.T)", "scale dropped"),
+    ("attention.py", "lse = np.where(seen, m_safe + np.log", "lse = np.where(seen, np.log", "lse drops max"),
+    ("attention.py", "(e @ v) / np.where", "(e @ v) * np.where", "normaliser inverted"),
+    ("layouts.py", "return p + a * N", "return p * N + a", "striped map"),
+    ("layouts.py", "(2 * N - 1 - p) * c + (a - c)", "(N + p) * c + (a - c)", "zigzag second chunk"),
+    ("layouts.py", "int((keys[None, :] <= qp[:, None]).sum())", "int((keys[None, :] < qp[:, None]).sum())",
+     "pair count off by one"),
+]
+
+
+def _load_mutant(tmp_path, idx, fname, old, new):
+    name = f"oracle_mutant_{idx}"
+    dst = tmp_path / name
+    shutil.copytree(ORACLE_DIR, dst, ignore=shutil.ignore_patterns("__pycache__"))
+    path = dst / fname
+    src = path.read_text()
+    assert old in src, f"mutation target not found in {fname}: {old!r}"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(name, dst / "__init__.py",
+                                                  submodule_search_locations=[str(dst)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[name] = mod
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("idx,mut", list(enumerate(MUTATIONS)), ids=[m[3] for m in MUTATIONS])
+def test_mutation_is_caught(tmp_path, idx, mut):
+    fname, old, new, _ = mut
+    mod = _load_mutant(tmp_path, idx, fname, old, new)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError, or the mutant crashing
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught the planted mistake: {mut[3]}"

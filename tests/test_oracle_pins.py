@@ -1,0 +1,11 @@
+"""The oracle against its pins (CPU only).  See tests/oracle_pins.py."""
+
+import pytest
+
+import oracle
+import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(oracle)
