@@ -1,0 +1,233 @@
+"""Ring-attention throughput on one MI355X, against the bf16 matrix-core roofline.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one ra_ring call: the whole simulated ring (all N virtual devices)
+over one batch of seeded synthetic input already resident in HBM.  The
+default workload is the Llama-3-8B-shaped causal ring: S = 32768 tokens over
+N = 8 virtual devices (blocks of 4096), 32 query / 8 key-value heads, head
+dim 128, bf16, contiguous layout.
+
+FLOPs are algorithmic: 4 * D per visible (query, key) pair per query head
+(2D for q.k, 2D for p.v), causal pairs counted exactly.  The printed JSON line
+carries value = TFLOP/s, the roofline object for the attention kernel (timed
+with HIP events on the stream it runs on) and the oracle's CPU rate on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+WORKLOADS = {
+    # name: (workload key in workloads.py, layout, device)
+    "gqa32k": ("gqa32k", "contiguous", -1),
+    "mha16k": ("mha16k", "contiguous", -1),
+    "gqa64k-contiguous": ("gqa64k", "contiguous", -1),
+    "gqa64k-striped": ("gqa64k", "striped", -1),
+    "gqa64k-zigzag": ("gqa64k", "zigzag", -1),
+    "share1m": ("share1m", "zigzag", 0),
+}
+
+
+def visible_pairs(S, N, layout, causal, device):
+    """Exact visible (query, key) pairs per query head (closed forms).
+
+    Whole ring: S^2 non-causal, S(S+1)/2 causal (every layout).  Device
+    share under zigzag causal: chunks c = S/2N; device p holds chunk p
+    (positions p*c + a, each sees p*c + a + 1 keys) and chunk 2N-1-p.
+    """
+    if device < 0:
+        return S * S if not causal else S * (S + 1) // 2
+    blk = S // N
+    if not causal:
+        return blk * S
+    if layout == "zigzag":
+        c = S // (2 * N)
+        first = sum_range(device * c + 1, device * c + c)
+        second = sum_range((2 * N - 1 - device) * c + 1, (2 * N - device) * c)
+        return first + second
+    if layout == "contiguous":
+        return sum_range(device * blk + 1, device * blk + blk)
+    return sum(device + a * N + 1 for a in range(blk))
+
+
+def sum_range(lo, hi):
+    return (lo + hi) * (hi - lo + 1) // 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target oracle time for the CPU baseline sample")
+    return ap.parse_args()
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(q, k, v, cfg, layout, device, seconds, gpu_out=None, gpu_lse=None):
+    """Oracle (fp64 numpy) on a growing seeded row sample until `seconds` pass."""
+    import oracle
+    from oracle import layouts as OL
+    import workloads
+
+    S, N, D, Hq = cfg["S"], cfg["N"], cfg["D"], cfg["Hq"]
+    Sq = q.shape[2]
+    causal = cfg["causal"]
+    if device >= 0:
+        qpos_all = OL.device_positions(S, N, layout, device)
+        kpos_all = OL.permuted_positions(S, N, layout)
+    else:
+        qpos_all, kpos_all = np.arange(S), np.arange(S)
+    rows_done, pairs, t_used = 0, 0, 0.0
+    errs = [0.0, 0.0]
+    seed = 1000
+    while t_used < seconds and rows_done < Sq * Hq:
+        sample = workloads.sample_rows(Hq, Sq, 32, seed)
+        seed += 1
+        rows = [(0, h, i) for (h, i) in sample]
+        t0 = time.perf_counter()
+        out, lse = oracle.attention_rows(q, k, v, rows, q_pos=qpos_all, k_pos=kpos_all,
+                                         causal=causal)
+        t_used += time.perf_counter() - t0
+        rows_done += len(rows)
+        for (_, h, i) in rows:
+            pairs += int(qpos_all[i]) + 1 if causal and device < 0 else (
+                int((kpos_all <= qpos_all[i]).sum()) if causal else len(kpos_all))
+        if gpu_out is not None:
+            for n, (_, h, i) in enumerate(rows):
+                go = gpu_out[0, h, i].float().numpy()
+                errs[0] = max(errs[0], float(np.abs(go - out[n]).max()))
+                errs[1] = max(errs[1], abs(float(gpu_lse[0, h, i]) - lse[n]))
+    flops = 4.0 * D * pairs
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{rows_done} seeded (head, row) pairs of the same workload, fp64 numpy, "
+                  f"{t_used:.1f} s; {pairs} visible pairs",
+    }, errs
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   f"(got {args.gpus})"}))
+        sys.exit(2)
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+    import workloads
+
+    ra.load()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    wkey, layout, device = WORKLOADS[args.workload]
+    cfg = workloads.WORKLOADS[wkey]
+    S, N, D, Hq, Hkv = cfg["S"], cfg["N"], cfg["D"], cfg["Hq"], cfg["Hkv"]
+    causal = cfg["causal"]
+    print(f"# generating inputs for {args.workload}", file=sys.stderr, flush=True)
+    q, k, v = workloads.workload_inputs(wkey)
+    if device >= 0:
+        pass  # share1m is drawn directly in device order (K, V) and local order (Q)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    nws = ra.ra_ring_workspace_bytes(qd, kd, N, layout, device)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ra.ra_ring(qd, kd, vd, out, lse, N, layout, causal, device, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1e3 / args.steps
+    pairs = visible_pairs(S, N, layout, causal, device)
+    flops = 4.0 * D * cfg["B"] * Hq * pairs
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    kern_ms = float(np.mean(ev_ms))
+    kern_tflops = flops / (kern_ms * 1e-3) / 1e12
+    q_tokens = qd.shape[2]
+    props = torch.cuda.get_device_properties(0)
+
+    cpu = None
+    errs = None
+    if not args.no_cpu_baseline:
+        print("# timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        cpu, errs = cpu_baseline(q, k, v, cfg, layout, device, args.cpu_seconds,
+                                 out.cpu(), lse.cpu())
+    line = {
+        "metric": "ring-attention TFLOP/s and % bf16 MFMA peak on 1 MI355X; tokens/s per ring",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "batch": cfg["B"], "seq_len": S, "ring_devices": N, "q_heads": Hq, "kv_heads": Hkv,
+            "head_dim": D, "causal": causal, "layout": layout, "device": device,
+            "query_tokens": q_tokens, "seed": cfg["seed"], "parallelism": "1 GPU, N virtual",
+        },
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(q_tokens / (ms_per_step * 1e-3), 1),
+        "algorithmic_tflop": round(flops / 1e12, 4),
+        "roofline": {
+            "bound": "mfma", "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel_ms": round(kern_ms, 4),
+        },
+        "cpu_baseline": cpu,
+        "sampled_max_err": None if errs is None else {"out": errs[0], "lse": errs[1]},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

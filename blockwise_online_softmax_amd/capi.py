@@ -1,0 +1,256 @@
+"""ctypes binding of libra.so: the C ABI of include/ra.h, same names.
+
+Argument marshalling only.  Tensors are PyTorch tensors on the GPU; the
+binding passes their data pointers and the current HIP stream and raises
+RuntimeError with ra_last_error() on a non-OK status.  Every computation
+runs in the library's HIP kernels; there is no other path.
+"""
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libra.so")
+
+RA_OK = 0
+RA_ERR_NULL = 1
+RA_ERR_SHAPE = 2
+RA_ERR_DTYPE = 3
+RA_ERR_ENUM = 4
+RA_ERR_UNSUPPORTED = 5
+RA_ERR_WORKSPACE = 6
+RA_ERR_HIP = 7
+STATUS_NAMES = {0: "RA_OK", 1: "RA_ERR_NULL", 2: "RA_ERR_SHAPE", 3: "RA_ERR_DTYPE",
+                4: "RA_ERR_ENUM", 5: "RA_ERR_UNSUPPORTED", 6: "RA_ERR_WORKSPACE",
+                7: "RA_ERR_HIP"}
+
+RA_F32 = 0
+RA_BF16 = 1
+RA_MASK_NONE = 0
+RA_MASK_CAUSAL = 1
+RA_CONTIGUOUS = 0
+RA_STRIPED = 1
+RA_ZIGZAG = 2
+LAYOUT_IDS = {"contiguous": RA_CONTIGUOUS, "striped": RA_STRIPED, "zigzag": RA_ZIGZAG}
+
+EXPORTED = ["ra_state_init", "ra_block_step", "ra_finalize", "ra_ring",
+            "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_last_error",
+            "ra_version"]
+
+
+class RaDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("Sq", ctypes.c_int64), ("Sk", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class RaState(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("acc", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Sq", ctypes.c_int64),
+                ("D", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path=None):
+    """Load libra.so (once).  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} not found: build the HIP library first "
+            "(python -m blockwise_online_softmax_amd.build)")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    dims_p, state_p = ctypes.POINTER(RaDims), ctypes.POINTER(RaState)
+    sigs = {
+        "ra_state_init": (i32, [state_p, vp]),
+        "ra_block_step": (i32, [vp, vp, vp, vp, vp, i32, dims_p, state_p, vp]),
+        "ra_finalize": (i32, [state_p, vp, vp, i32, vp]),
+        "ra_ring": (i32, [vp, vp, vp, vp, vp, dims_p, i32, i32, i32, i32, vp, sz, vp]),
+        "ra_ring_workspace_bytes": (sz, [dims_p, i32, i32, i32]),
+        "ra_permute": (i32, [vp, vp, i64, i64, i64, i32, i32, i32, vp]),
+        "ra_positions": (i32, [vp, i64, i32, i32, i32, vp]),
+        "ra_last_error": (ctypes.c_char_p, []),
+        "ra_version": (i32, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error():
+    return load().ra_last_error().decode()
+
+
+def _check(status, what):
+    if status != RA_OK:
+        raise RuntimeError(f"{what} failed: {STATUS_NAMES.get(status, status)}: {last_error()}")
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_id(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_dims(q, k, scale=None):
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch / head dim")
+    return RaDims(B, Hq, Hkv, Sq, Sk, D, _dtype_id(q), 0.0 if scale is None else float(scale))
+
+
+class State:
+    """Caller-owned running state (fp32 m, l, acc) of a query block."""
+
+    def __init__(self, B, Hq, Sq, D, device="cuda"):
+        torch = _torch()
+        self.m = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device)
+        self.l = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device)
+        self.acc = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=device)
+        self.shape = (B, Hq, Sq, D)
+
+    def c_struct(self):
+        B, Hq, Sq, D = self.shape
+        return RaState(self.m.data_ptr(), self.l.data_ptr(), self.acc.data_ptr(), B, Hq, Sq, D)
+
+
+# ---------------------------------------------------------------------------
+# the ABI calls
+
+
+def ra_state_init(state, stream=None):
+    st = state.c_struct()
+    _check(load().ra_state_init(ctypes.byref(st), _stream(stream)), "ra_state_init")
+
+
+def ra_block_step(Q_i, K_j, V_j, q_pos, k_pos, mask_mode, state, scale=None, stream=None):
+    for t, n in ((Q_i, "Q_i"), (K_j, "K_j"), (V_j, "V_j")):
+        _require(t, n, Q_i.dtype)
+    torch = _torch()
+    if mask_mode == RA_MASK_CAUSAL:
+        _require(q_pos, "q_pos", torch.int32)
+        _require(k_pos, "k_pos", torch.int32)
+    d = make_dims(Q_i, K_j, scale)
+    st = state.c_struct()
+    _check(load().ra_block_step(_ptr(Q_i), _ptr(K_j), _ptr(V_j), _ptr(q_pos), _ptr(k_pos),
+                                int(mask_mode), ctypes.byref(d), ctypes.byref(st),
+                                _stream(stream)), "ra_block_step")
+
+
+def ra_finalize(state, out, lse=None, stream=None):
+    _require(out, "out")
+    if lse is not None:
+        _require(lse, "lse", _torch().float32)
+    st = state.c_struct()
+    _check(load().ra_finalize(ctypes.byref(st), _ptr(out), _ptr(lse), _dtype_id(out),
+                              _stream(stream)), "ra_finalize")
+
+
+def ra_ring_workspace_bytes(q, k, N, layout, device=-1, scale=None):
+    d = make_dims(q, k, scale)
+    n = load().ra_ring_workspace_bytes(ctypes.byref(d), int(N), LAYOUT_IDS.get(layout, layout),
+                                       int(device))
+    if n == ctypes.c_size_t(-1).value:
+        raise RuntimeError(f"ra_ring_workspace_bytes: {last_error()}")
+    return int(n)
+
+
+def ra_ring(Q, K, V, out, lse, N, layout="contiguous", causal=False, device=-1, ws=None,
+            scale=None, stream=None):
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (out, "out")):
+        _require(t, n, Q.dtype)
+    _require(lse, "lse", _torch().float32)
+    if ws is not None:
+        _require(ws, "ws")
+    d = make_dims(Q, K, scale)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().ra_ring(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), ctypes.byref(d),
+                          int(N), LAYOUT_IDS.get(layout, layout), int(bool(causal)), int(device),
+                          _ptr(ws), wsb, _stream(stream)), "ra_ring")
+
+
+def ra_permute(src, dst, N, layout, inverse=False, stream=None):
+    """src, dst: [outer, S, ...] tensors; rows are everything after the S axis."""
+    _require(src, "src")
+    _require(dst, "dst", src.dtype)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst shapes differ")
+    outer = src.shape[0]
+    S = src.shape[1]
+    row_bytes = src.element_size() * math.prod(src.shape[2:])
+    _check(load().ra_permute(_ptr(src), _ptr(dst), outer, S, row_bytes, int(N),
+                             LAYOUT_IDS.get(layout, layout), int(bool(inverse)), _stream(stream)),
+           "ra_permute")
+
+
+def ra_positions(pos, S, N, layout, device=-1, stream=None):
+    _require(pos, "pos", _torch().int32)
+    _check(load().ra_positions(_ptr(pos), int(S), int(N), LAYOUT_IDS.get(layout, layout),
+                               int(device), _stream(stream)), "ra_positions")
+
+
+def ra_version():
+    return int(load().ra_version())
+
+
+# ---------------------------------------------------------------------------
+# allocation conveniences (plumbing: torch allocates, the library computes)
+
+
+def ring_attention(Q, K, V, N, layout="contiguous", causal=False, device=-1, scale=None,
+                   stream=None):
+    """Allocate out / lse / workspace with torch and call ra_ring."""
+    torch = _torch()
+    out = torch.empty_like(Q)
+    lse = torch.empty(Q.shape[:3], dtype=torch.float32, device=Q.device)
+    nws = ra_ring_workspace_bytes(Q, K, N, layout, device, scale)
+    ws = torch.empty(nws, dtype=torch.uint8, device=Q.device) if nws > 0 else None
+    ra_ring(Q, K, V, out, lse, N, layout, causal, device, ws, scale, stream)
+    return out, lse

@@ -1,0 +1,349 @@
+// C ABI of libra.so (declared in include/ra.h): argument validation on the
+// host, workspace layout and kernel dispatch.  Validation runs before any HIP
+// call, so every error path is reachable without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ra_status fail(ra_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ra_status ok() {
+  g_err[0] = '\0';
+  return RA_OK;
+}
+
+ra_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return RA_OK;
+}
+
+constexpr int64_t kMaxSeq = (int64_t)1 << 31;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+int64_t elem_size(int dtype) { return dtype == RA_BF16 ? 2 : 4; }
+bool head_dim_ok(int64_t D) { return D == 8 || D == 16 || D == 32 || D == 64 || D == 128; }
+bool layout_ok(int layout) {
+  return layout == RA_CONTIGUOUS || layout == RA_STRIPED || layout == RA_ZIGZAG;
+}
+int64_t round256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+ra_status check_dims(const ra_dims* d) {
+  if (d == nullptr) return fail(RA_ERR_NULL, "dims is NULL");
+  if (d->dtype != RA_F32 && d->dtype != RA_BF16)
+    return fail(RA_ERR_DTYPE, "unknown dtype %d", (int)d->dtype);
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->Sq < 1 || d->Sk < 1 || d->D < 1)
+    return fail(RA_ERR_SHAPE, "all sizes must be >= 1 (B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld)",
+                (long long)d->B, (long long)d->Hq, (long long)d->Hkv, (long long)d->Sq,
+                (long long)d->Sk, (long long)d->D);
+  if (d->Hq % d->Hkv != 0)
+    return fail(RA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)d->Hq,
+                (long long)d->Hkv);
+  if (!head_dim_ok(d->D))
+    return fail(RA_ERR_UNSUPPORTED, "head dim %lld not supported (8, 16, 32, 64, 128)",
+                (long long)d->D);
+  if (d->Sq >= kMaxSeq || d->Sk >= kMaxSeq)
+    return fail(RA_ERR_SHAPE, "sequence lengths must be < 2^31");
+  if (d->B * d->Hq >= kMaxSeq || d->B * d->Hq * d->Sq >= ((int64_t)1 << 40))
+    return fail(RA_ERR_SHAPE, "batch x heads x rows too large");
+  if (!(d->scale == d->scale) || isinf(d->scale))
+    return fail(RA_ERR_SHAPE, "scale must be finite");
+  return RA_OK;
+}
+
+float effective_scale(const ra_dims* d) {
+  return d->scale > 0.f ? d->scale : (float)(1.0 / sqrt((double)d->D));
+}
+
+ra_status check_state(const ra_state* st) {
+  if (st == nullptr) return fail(RA_ERR_NULL, "state is NULL");
+  if (st->m == nullptr || st->l == nullptr || st->acc == nullptr)
+    return fail(RA_ERR_NULL, "state buffers m, l, acc must be non-NULL");
+  if (st->B < 1 || st->Hq < 1 || st->Sq < 1 || st->Sq >= kMaxSeq)
+    return fail(RA_ERR_SHAPE, "state sizes out of range");
+  if (!head_dim_ok(st->D))
+    return fail(RA_ERR_UNSUPPORTED, "state head dim %lld not supported", (long long)st->D);
+  if (!aligned(st->m, 4) || !aligned(st->l, 4) || !aligned(st->acc, 16))
+    return fail(RA_ERR_SHAPE, "state buffers misaligned (acc needs 16 bytes)");
+  return RA_OK;
+}
+
+ra_status check_ring_args(const ra_dims* d, int N, int layout, int device) {
+  ra_status s = check_dims(d);
+  if (s != RA_OK) return s;
+  if (N < 1) return fail(RA_ERR_SHAPE, "N must be >= 1 (got %d)", N);
+  if (!layout_ok(layout)) return fail(RA_ERR_ENUM, "unknown layout %d", layout);
+  if (device < -1 || device >= N)
+    return fail(RA_ERR_ENUM, "device must be -1 or in [0, N) (got %d, N=%d)", device, N);
+  const int64_t S = d->Sk;
+  if (S % N != 0) return fail(RA_ERR_SHAPE, "S=%lld not divisible by N=%d", (long long)S, N);
+  if (layout == RA_ZIGZAG && S % (2 * (int64_t)N) != 0)
+    return fail(RA_ERR_SHAPE, "zigzag needs S %% 2N == 0 (S=%lld N=%d)", (long long)S, N);
+  if (device < 0 && d->Sq != S)
+    return fail(RA_ERR_SHAPE, "whole ring needs Sq == Sk (Sq=%lld Sk=%lld)", (long long)d->Sq,
+                (long long)S);
+  if (device >= 0 && d->Sq != S / N)
+    return fail(RA_ERR_SHAPE, "device share needs Sq == S/N (Sq=%lld S/N=%lld)",
+                (long long)d->Sq, (long long)(S / N));
+  return RA_OK;
+}
+
+struct WsLayout {
+  int64_t q, k, v, out, lse, total;
+};
+
+WsLayout ring_ws(const ra_dims* d, int layout, int device) {
+  WsLayout w = {0, 0, 0, 0, 0, 0};
+  if (device >= 0 || layout == RA_CONTIGUOUS) return w;
+  const int64_t es = elem_size(d->dtype);
+  const int64_t S = d->Sk;
+  const int64_t qb = round256(d->B * d->Hq * S * d->D * es);
+  const int64_t kb = round256(d->B * d->Hkv * S * d->D * es);
+  const int64_t lb = round256(d->B * d->Hq * S * 4);
+  w.q = 0;
+  w.k = w.q + qb;
+  w.v = w.k + kb;
+  w.out = w.v + kb;
+  w.lse = w.out + qb;
+  w.total = w.lse + lb;
+  return w;
+}
+
+ra::AttnParams base_params(const ra_dims* d) {
+  ra::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = (int)d->B;
+  p.Hq = (int)d->Hq;
+  p.Hkv = (int)d->Hkv;
+  p.scale = effective_scale(d);
+  p.sl2 = (float)((double)p.scale * 1.4426950408889634074);
+  p.layout = RA_CONTIGUOUS;
+  p.N = 1;
+  return p;
+}
+
+hipError_t launch_attention(const ra::AttnParams& p, int D, int dtype, bool causal, int pos_mode,
+                            bool state_io, hipStream_t s) {
+  if (dtype == RA_BF16 && ra::mfma_supports(D))
+    return ra::launch_attn_mfma(p, D, causal, pos_mode, state_io, s);
+  return ra::launch_attn_valu(p, D, dtype, causal, pos_mode, state_io, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_version(void) { return 100; }
+
+const char* ra_last_error(void) { return g_err; }
+
+ra_status ra_state_init(const ra_state* st, void* stream) {
+  ra_status s = check_state(st);
+  if (s != RA_OK) return s;
+  (void)hipGetLastError();
+  s = hip_status(ra::launch_state_init(st->m, st->l, st->acc, st->B * st->Hq * st->Sq, st->D,
+                                       (hipStream_t)stream),
+                 "ra_state_init launch");
+  return s == RA_OK ? ok() : s;
+}
+
+ra_status ra_block_step(const void* Q_i, const void* K_j, const void* V_j, const int32_t* q_pos,
+                        const int32_t* k_pos, ra_mask mask_mode, const ra_dims* d,
+                        const ra_state* st, void* stream) {
+  ra_status s = check_dims(d);
+  if (s != RA_OK) return s;
+  s = check_state(st);
+  if (s != RA_OK) return s;
+  if (mask_mode != RA_MASK_NONE && mask_mode != RA_MASK_CAUSAL)
+    return fail(RA_ERR_ENUM, "unknown mask mode %d", (int)mask_mode);
+  if (Q_i == nullptr || K_j == nullptr || V_j == nullptr)
+    return fail(RA_ERR_NULL, "Q_i, K_j and V_j must be non-NULL");
+  if (mask_mode == RA_MASK_CAUSAL && (q_pos == nullptr || k_pos == nullptr))
+    return fail(RA_ERR_NULL, "causal mask needs q_pos and k_pos");
+  if (st->B != d->B || st->Hq != d->Hq || st->Sq != d->Sq || st->D != d->D)
+    return fail(RA_ERR_SHAPE, "state (B=%lld Hq=%lld Sq=%lld D=%lld) does not match dims",
+                (long long)st->B, (long long)st->Hq, (long long)st->Sq, (long long)st->D);
+  if (!aligned(Q_i, 16) || !aligned(K_j, 16) || !aligned(V_j, 16))
+    return fail(RA_ERR_SHAPE, "Q_i, K_j, V_j must be 16-byte aligned");
+  ra::AttnParams p = base_params(d);
+  p.Q = Q_i;
+  p.K = K_j;
+  p.V = V_j;
+  p.q_pos = q_pos;
+  p.k_pos = k_pos;
+  p.m = st->m;
+  p.l = st->l;
+  p.acc = st->acc;
+  p.Sq_tot = d->Sq;
+  p.Sk_tot = d->Sk;
+  p.nqblk = 1;
+  p.qlen = (int)d->Sq;
+  p.dev0 = 0;
+  p.nkblk = 1;
+  p.klen = (int)d->Sk;
+  p.blk = (int)d->Sk;
+  const bool causal = mask_mode == RA_MASK_CAUSAL;
+  (void)hipGetLastError();
+  s = hip_status(launch_attention(p, (int)d->D, d->dtype, causal,
+                                  causal ? ra::POS_ARRAY : ra::POS_NONE, true, (hipStream_t)stream),
+                 "ra_block_step launch");
+  return s == RA_OK ? ok() : s;
+}
+
+ra_status ra_finalize(const ra_state* st, void* out, float* lse, ra_dtype out_dtype,
+                      void* stream) {
+  ra_status s = check_state(st);
+  if (s != RA_OK) return s;
+  if (out == nullptr) return fail(RA_ERR_NULL, "out must be non-NULL");
+  if (out_dtype != RA_F32 && out_dtype != RA_BF16)
+    return fail(RA_ERR_DTYPE, "unknown out dtype %d", (int)out_dtype);
+  if (!aligned(out, out_dtype == RA_BF16 ? 8 : 16) || (lse != nullptr && !aligned(lse, 4)))
+    return fail(RA_ERR_SHAPE, "out / lse misaligned");
+  (void)hipGetLastError();
+  s = hip_status(ra::launch_finalize(st->m, st->l, st->acc, out, lse, st->B * st->Hq * st->Sq,
+                                     st->D, out_dtype, (hipStream_t)stream),
+                 "ra_finalize launch");
+  return s == RA_OK ? ok() : s;
+}
+
+size_t ra_ring_workspace_bytes(const ra_dims* d, int N, ra_layout layout, int device) {
+  if (check_ring_args(d, N, layout, device) != RA_OK) return (size_t)-1;
+  ok();
+  return (size_t)ring_ws(d, layout, device).total;
+}
+
+ra_status ra_ring(const void* Q, const void* K, const void* V, void* out, float* lse,
+                  const ra_dims* d, int N, ra_layout layout, int causal, int device, void* ws,
+                  size_t ws_bytes, void* stream) {
+  ra_status s = check_ring_args(d, N, layout, device);
+  if (s != RA_OK) return s;
+  if (causal != 0 && causal != 1) return fail(RA_ERR_ENUM, "causal must be 0 or 1 (got %d)", causal);
+  if (Q == nullptr || K == nullptr || V == nullptr || out == nullptr || lse == nullptr)
+    return fail(RA_ERR_NULL, "Q, K, V, out and lse must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4))
+    return fail(RA_ERR_SHAPE, "Q, K, V, out must be 16-byte aligned and lse 4-byte aligned");
+  const WsLayout w = ring_ws(d, layout, device);
+  if (w.total > 0) {
+    if (ws == nullptr) return fail(RA_ERR_WORKSPACE, "workspace of %lld bytes required",
+                                   (long long)w.total);
+    if ((int64_t)ws_bytes < w.total)
+      return fail(RA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", ws_bytes,
+                  (long long)w.total);
+    if (!aligned(ws, 256)) return fail(RA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t S = d->Sk;
+  const int blk = (int)(S / N);
+  const int64_t es = elem_size(d->dtype);
+  const int64_t row_bytes = d->D * es;
+
+  ra::AttnParams p = base_params(d);
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.out = out;
+  p.lse = lse;
+  p.layout = layout;
+  p.N = N;
+  p.blk = blk;
+  p.nkblk = N;
+  p.klen = blk;
+  p.Sk_tot = S;
+  if (device >= 0) {
+    p.Sq_tot = blk;
+    p.nqblk = 1;
+    p.qlen = blk;
+    p.dev0 = device;
+  } else {
+    p.Sq_tot = S;
+    p.nqblk = N;
+    p.qlen = blk;
+    p.dev0 = 0;
+  }
+
+  (void)hipGetLastError();
+  char* wsb = (char*)ws;
+  const bool permuted = w.total > 0;
+  if (permuted) {
+    s = hip_status(ra::launch_permute(Q, wsb + w.q, d->B * d->Hq, S, row_bytes, N, layout, 0, st),
+                   "permute Q");
+    if (s != RA_OK) return s;
+    s = hip_status(ra::launch_permute(K, wsb + w.k, d->B * d->Hkv, S, row_bytes, N, layout, 0, st),
+                   "permute K");
+    if (s != RA_OK) return s;
+    s = hip_status(ra::launch_permute(V, wsb + w.v, d->B * d->Hkv, S, row_bytes, N, layout, 0, st),
+                   "permute V");
+    if (s != RA_OK) return s;
+    p.Q = wsb + w.q;
+    p.K = wsb + w.k;
+    p.V = wsb + w.v;
+    p.out = wsb + w.out;
+    p.lse = (float*)(wsb + w.lse);
+  }
+  s = hip_status(launch_attention(p, (int)d->D, d->dtype, causal != 0,
+                                  causal ? ra::POS_ANALYTIC : ra::POS_NONE, false, st),
+                 "ring attention launch");
+  if (s != RA_OK) return s;
+  if (permuted) {
+    s = hip_status(ra::launch_permute(wsb + w.out, out, d->B * d->Hq, S, row_bytes, N, layout, 1,
+                                      st),
+                   "un-permute out");
+    if (s != RA_OK) return s;
+    s = hip_status(ra::launch_permute(wsb + w.lse, lse, d->B * d->Hq, S, 4, N, layout, 1, st),
+                   "un-permute lse");
+    if (s != RA_OK) return s;
+  }
+  return ok();
+}
+
+ra_status ra_permute(const void* src, void* dst, int64_t outer, int64_t S, int64_t row_bytes,
+                     int N, ra_layout layout, int inverse, void* stream) {
+  if (src == nullptr || dst == nullptr) return fail(RA_ERR_NULL, "src and dst must be non-NULL");
+  if (!layout_ok(layout)) return fail(RA_ERR_ENUM, "unknown layout %d", (int)layout);
+  if (inverse != 0 && inverse != 1) return fail(RA_ERR_ENUM, "inverse must be 0 or 1");
+  if (outer < 1 || S < 1 || S >= kMaxSeq || N < 1)
+    return fail(RA_ERR_SHAPE, "outer, S, N must be >= 1 and S < 2^31");
+  if (row_bytes < 4 || row_bytes % 4 != 0)
+    return fail(RA_ERR_SHAPE, "row_bytes must be a positive multiple of 4 (got %lld)",
+                (long long)row_bytes);
+  if (S % N != 0) return fail(RA_ERR_SHAPE, "S=%lld not divisible by N=%d", (long long)S, N);
+  if (layout == RA_ZIGZAG && S % (2 * (int64_t)N) != 0)
+    return fail(RA_ERR_SHAPE, "zigzag needs S %% 2N == 0");
+  const uintptr_t al = row_bytes % 16 == 0 ? 16 : 4;
+  if (!aligned(src, al) || !aligned(dst, al)) return fail(RA_ERR_SHAPE, "src / dst misaligned");
+  (void)hipGetLastError();
+  ra_status s = hip_status(ra::launch_permute(src, dst, outer, S, row_bytes, N, layout, inverse,
+                                              (hipStream_t)stream),
+                           "ra_permute launch");
+  return s == RA_OK ? ok() : s;
+}
+
+ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int device,
+                       void* stream) {
+  if (pos == nullptr) return fail(RA_ERR_NULL, "pos must be non-NULL");
+  if (!layout_ok(layout)) return fail(RA_ERR_ENUM, "unknown layout %d", (int)layout);
+  if (S < 1 || S >= kMaxSeq || N < 1) return fail(RA_ERR_SHAPE, "S, N must be >= 1, S < 2^31");
+  if (device < -1 || device >= N) return fail(RA_ERR_ENUM, "device must be -1 or in [0, N)");
+  if (S % N != 0) return fail(RA_ERR_SHAPE, "S not divisible by N");
+  if (layout == RA_ZIGZAG && S % (2 * (int64_t)N) != 0)
+    return fail(RA_ERR_SHAPE, "zigzag needs S %% 2N == 0");
+  (void)hipGetLastError();
+  ra_status s = hip_status(ra::launch_positions(pos, S, N, layout, device, (hipStream_t)stream),
+                           "ra_positions launch");
+  return s == RA_OK ? ok() : s;
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+/*
+ * ra.h -- C ABI of the MI355X (gfx950) ring-attention library, libra.so.
+ *
+ * One device's share of ring (sequence-parallel) attention, and a whole ring
+ * simulated on one GPU.  A resident query block keeps, per query row, a
+ * running max m, a running denominator l and an unnormalised output acc; each
+ * key/value block that arrives is folded in with exponential rescaling, and
+ * after the last block out = acc / l.  The operation and its notation follow
+ *   "Module 23: Distributed Training", sections "Sequence Parallelism: Ring
+ *   Attention" and "The Math: One Block at a Time" (the fold and the final
+ *   division), "Exact by Construction" (causal ring = causally masked full
+ *   attention), "The Causal Imbalance -- and the Striped Fix" (layouts);
+ *   "Explain ring attention and how it enables very long contexts across
+ *   multiple devices?", section "The ring" (split / compute / pass / repeat
+ *   and divide, and the rotation order);
+ *   "3.6 Distributed Training II: Tensor, Pipeline, Sequence & Expert
+ *   Parallelism", section "Ring Attention" (per-step loop on a device) and
+ *   "Vocab-parallel cross-entropy" (log-sum-exp = m + log Z).
+ *
+ * Conventions shared by every call
+ *   - Every tensor and workspace is device memory owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after a call returns.
+ *   - Tensors are dense and row-major with the head dim innermost:
+ *       Q, out      [B, Hq,  Sq, D]      K, V   [B, Hkv, Sk, D]
+ *       m, l, lse   [B, Hq,  Sq]  fp32   acc    [B, Hq,  Sq, D] fp32
+ *     Q, K, V (and out, unless stated) share one element type (ra_dtype).
+ *     Device pointers must be 16-byte aligned.
+ *   - Query head h reads key/value head h / (Hq / Hkv) (contiguous groups).
+ *   - Scores are s = (q . k) * scale; scale <= 0 selects 1/sqrt(D).
+ *   - Causal masking is on global token positions: key j is visible to
+ *     query i iff pos(j) <= pos(i) (the diagonal is visible).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous on it; none synchronises the device.
+ *   - Every argument is validated on the host before anything is launched;
+ *     on error nothing is launched, the call returns a non-zero ra_status and
+ *     ra_last_error() describes the problem.  No exception crosses the ABI.
+ *   - Supported head dims: D in {8, 16, 32, 64, 128}.  bf16 with D in
+ *     {32, 64, 128} runs on the matrix cores (bf16 MFMA, fp32 accumulate);
+ *     other cases run on a vector-ALU kernel.  Sequence lengths < 2^31.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  RA_ERR_SHAPE = 2,       /* sizes inconsistent, not divisible, misaligned   */
+  RA_ERR_DTYPE = 3,       /* unknown element type                            */
+  RA_ERR_ENUM = 4,        /* unknown mask / layout value, bad device index   */
+  RA_ERR_UNSUPPORTED = 5, /* valid but not built (head dim)                  */
+  RA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required      */
+  RA_ERR_HIP = 7          /* the HIP runtime reported an error on launch     */
+} ra_status;
+
+typedef enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+typedef enum ra_mask { RA_MASK_NONE = 0, RA_MASK_CAUSAL = 1 } ra_mask;
+
+/* Token -> device layouts of a sequence of S tokens over N devices
+ * (blk = S/N tokens each; local index a = 0..blk-1, ascending positions):
+ *   RA_CONTIGUOUS  device p holds block p:        pos = p*blk + a
+ *   RA_STRIPED     device p holds p, p+N, ...:    pos = p + a*N
+ *   RA_ZIGZAG      2N chunks of c = S/(2N); device p holds chunk p and then
+ *                  chunk 2N-1-p:  a < c: pos = p*c + a,
+ *                                 a >= c: pos = (2N-1-p)*c + (a-c)
+ *                  (needs S % 2N == 0).
+ * "Device order" concatenates the N device blocks, device 0 first. */
+typedef enum ra_layout { RA_CONTIGUOUS = 0, RA_STRIPED = 1, RA_ZIGZAG = 2 } ra_layout;
+
+typedef struct ra_dims {
+  int64_t B, Hq, Hkv; /* batch, query heads, key/value heads (Hq % Hkv == 0) */
+  int64_t Sq, Sk;     /* query rows and key rows per (batch, head)           */
+  int64_t D;          /* head dim                                            */
+  int32_t dtype;      /* ra_dtype of Q, K, V                                 */
+  float scale;        /* score scale; <= 0 means 1/sqrt(D)                   */
+} ra_dims;
+
+/* Running state of a query block (fp32, caller-owned device buffers).
+ * m[r] is the running max of the scaled scores seen by row r, l[r] the sum of
+ * exp(s - m[r]) over them and acc[r, :] the sum of exp(s - m[r]) * v.  A row
+ * that has seen no visible key has m = -inf, l = 0, acc = 0. */
+typedef struct ra_state {
+  float* m;   /* [B, Hq, Sq]    */
+  float* l;   /* [B, Hq, Sq]    */
+  float* acc; /* [B, Hq, Sq, D] */
+  int64_t B, Hq, Sq, D;
+} ra_state;
+
+/* The empty state: m = -inf, l = 0, acc = 0.  ("Explain ring attention...",
+ * "The ring": the running max starts at -inf, sum and output at zero.) */
+ra_status ra_state_init(const ra_state* st, void* stream);
+
+/* Fold one key/value block into the state in place ("Module 23", "The Math:
+ * One Block at a Time"): for each row, m' = max(m, max_j s_ij),
+ * l = l*e^(m-m') + sum_j e^(s_ij-m'), acc = acc*e^(m-m') + sum_j e^(s_ij-m') v_j.
+ *   Q_i [B,Hq,Sq,D], K_j / V_j [B,Hkv,Sk,D] of d->dtype; d describes them and
+ *   must match st (B, Hq, Sq, D).
+ *   q_pos [Sq], k_pos [Sk]: int32 global positions (shared over batch and
+ *   heads); read only for RA_MASK_CAUSAL, may be NULL for RA_MASK_NONE.
+ *   Masked pairs contribute nothing; a row with no visible key in this block
+ *   keeps its state.  The stored m is the exact running max. */
+ra_status ra_block_step(const void* Q_i, const void* K_j, const void* V_j,
+                        const int32_t* q_pos, const int32_t* k_pos, ra_mask mask_mode,
+                        const ra_dims* d, const ra_state* st, void* stream);
+
+/* out = acc / l in out_dtype (round to nearest even for bf16) and
+ * lse = m + ln l in fp32 ("Module 23", "The Math": divide at the end;
+ * "3.6 ...", "Vocab-parallel cross-entropy": logsumexp = m + log Z).
+ * A row with l == 0 gets out = 0 and lse = -inf.  lse may be NULL. */
+ra_status ra_finalize(const ra_state* st, void* out, float* lse, ra_dtype out_dtype,
+                      void* stream);
+
+/* The whole ring ("Explain ring attention...", "The ring"): the sequence is
+ * split over N virtual devices by `layout`; each device keeps its query block
+ * and folds in the N key/value blocks in ring order -- at step s device p
+ * holds block (p - s) mod N -- then divides by l.  Blocks (and tiles) with no
+ * visible pair are skipped.  Outputs: out (Q's dtype) and lse (fp32).
+ *   device == -1: the whole ring on this GPU.  Q, K, V, out, lse are in
+ *     natural token order; d->Sq == d->Sk == S.  Striped and zigzag layouts
+ *     are permuted into device order in the workspace and back afterwards.
+ *   device == p (0 <= p < N): device p's share.  Q is p's block in its local
+ *     order (d->Sq == S/N), K and V are the whole sequence in device order
+ *     (d->Sk == S), and out / lse come back in p's local order.
+ *   causal: 0 or 1.  S % N == 0 (S % 2N == 0 for zigzag).
+ *   ws / ws_bytes: workspace of at least ra_ring_workspace_bytes(...) bytes
+ *   (0 for contiguous layouts and for device >= 0; ws may then be NULL). */
+ra_status ra_ring(const void* Q, const void* K, const void* V, void* out, float* lse,
+                  const ra_dims* d, int N, ra_layout layout, int causal, int device,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes ra_ring needs for these arguments; (size_t)-1 on invalid
+ * arguments (ra_last_error() says why). */
+size_t ra_ring_workspace_bytes(const ra_dims* d, int N, ra_layout layout, int device);
+
+/* Layout permutation of rows ("Module 23", "The Causal Imbalance -- and the
+ * Striped Fix"): src and dst are [outer, S, row_bytes] byte arrays.
+ *   inverse == 0: natural -> device order, dst[o][p*blk + a] = src[o][pos(p, a)]
+ *   inverse == 1: device -> natural order, dst[o][pos(p, a)] = src[o][p*blk + a]
+ * row_bytes must be a positive multiple of 4 (16 or more runs vectorised).
+ * src and dst must not overlap. */
+ra_status ra_permute(const void* src, void* dst, int64_t outer, int64_t S, int64_t row_bytes,
+                     int N, ra_layout layout, int inverse, void* stream);
+
+/* int32 global positions.  device == -1: pos[i] for every index i of a
+ * device-ordered sequence (S entries).  device == p: p's block in its local
+ * order (S/N entries). */
+ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int device,
+                       void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ra_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -1,0 +1,156 @@
+"""The C ABI on the host, no GPU: libra.so loads, exports every function
+include/ra.h declares, and every invalid-argument path returns its status and
+a message before anything is launched (validation never touches the device,
+so fake but aligned device addresses are safe here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from blockwise_online_softmax_amd import capi
+from blockwise_online_softmax_amd.capi import RaDims, RaState
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+FAKE = 0x7F0000000000  # aligned, never dereferenced: validation rejects first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(capi.LIB_PATH):
+        pytest.fail("libra.so not built: run python -m blockwise_online_softmax_amd.build")
+    return capi.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(capi.EXPORTED), names
+    dyn = subprocess.run(["nm", "-D", "--defined-only", capi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ra_[a-z_]+)\b", dyn))
+    for n in names:
+        assert n in exported, f"{n} not exported"
+        assert getattr(lib, n) is not None
+    assert lib.ra_version() == 100
+
+
+def dims(B=1, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, dtype=1, scale=0.0):
+    return RaDims(B, Hq, Hkv, Sq, Sk, D, dtype, scale)
+
+
+def state(B=1, Hq=4, Sq=128, D=128, m=FAKE, l=FAKE + 4096, acc=FAKE + 8192):
+    return RaState(m, l, acc, B, Hq, Sq, D)
+
+
+def expect(status, code, fragment):
+    assert status == code, (capi.STATUS_NAMES.get(status), capi.last_error())
+    assert fragment.lower() in capi.last_error().lower(), capi.last_error()
+
+
+def step(lib, d, st, mask=0, q=FAKE, k=FAKE, v=FAKE, qp=FAKE, kp=FAKE):
+    return lib.ra_block_step(q, k, v, qp, kp, mask, ctypes.byref(d) if d is not None else None,
+                             ctypes.byref(st) if st is not None else None, None)
+
+
+def test_state_init_errors(lib):
+    expect(lib.ra_state_init(None, None), capi.RA_ERR_NULL, "state")
+    expect(lib.ra_state_init(ctypes.byref(state(m=0)), None), capi.RA_ERR_NULL, "non-NULL")
+    expect(lib.ra_state_init(ctypes.byref(state(D=100)), None), capi.RA_ERR_UNSUPPORTED, "head dim")
+    expect(lib.ra_state_init(ctypes.byref(state(Sq=0)), None), capi.RA_ERR_SHAPE, "range")
+    expect(lib.ra_state_init(ctypes.byref(state(acc=FAKE + 8)), None), capi.RA_ERR_SHAPE, "align")
+
+
+def test_block_step_errors(lib):
+    st = state()
+    expect(step(lib, None, st), capi.RA_ERR_NULL, "dims")
+    expect(step(lib, dims(dtype=5), st), capi.RA_ERR_DTYPE, "dtype")
+    expect(step(lib, dims(Hq=3), state(Hq=3)), capi.RA_ERR_SHAPE, "multiple")
+    expect(step(lib, dims(D=48), state(D=48)), capi.RA_ERR_UNSUPPORTED, "head dim")
+    expect(step(lib, dims(), st, mask=3), capi.RA_ERR_ENUM, "mask")
+    expect(step(lib, dims(), st, mask=1, qp=None), capi.RA_ERR_NULL, "q_pos")
+    expect(step(lib, dims(), st, q=None), capi.RA_ERR_NULL, "non-NULL")
+    expect(step(lib, dims(Sq=64), st), capi.RA_ERR_SHAPE, "does not match")
+    expect(step(lib, dims(), st, q=FAKE + 2), capi.RA_ERR_SHAPE, "aligned")
+    expect(step(lib, dims(Sk=0), st), capi.RA_ERR_SHAPE, ">= 1")
+    expect(step(lib, dims(scale=float("nan")), st), capi.RA_ERR_SHAPE, "finite")
+    expect(step(lib, dims(Sq=1 << 31), state(Sq=1 << 31)), capi.RA_ERR_SHAPE, "2^31")
+
+
+def test_finalize_errors(lib):
+    st = state()
+    expect(lib.ra_finalize(ctypes.byref(st), None, None, 1, None), capi.RA_ERR_NULL, "out")
+    expect(lib.ra_finalize(ctypes.byref(st), FAKE, None, 9, None), capi.RA_ERR_DTYPE, "dtype")
+    expect(lib.ra_finalize(None, FAKE, None, 1, None), capi.RA_ERR_NULL, "state")
+    expect(lib.ra_finalize(ctypes.byref(st), FAKE + 2, None, 1, None), capi.RA_ERR_SHAPE, "align")
+
+
+def ring(lib, d, N=8, layout=0, causal=1, device=-1, ws=None, wsb=0, out=FAKE, lse=FAKE):
+    return lib.ra_ring(FAKE, FAKE, FAKE, out, lse, ctypes.byref(d), N, layout, causal, device,
+                       ws, wsb, None)
+
+
+def test_ring_errors(lib):
+    expect(ring(lib, dims(), N=0), capi.RA_ERR_SHAPE, "N must")
+    expect(ring(lib, dims(), layout=7), capi.RA_ERR_ENUM, "layout")
+    expect(ring(lib, dims(), device=8), capi.RA_ERR_ENUM, "device")
+    expect(ring(lib, dims(), device=-2), capi.RA_ERR_ENUM, "device")
+    expect(ring(lib, dims(Sq=120, Sk=120), N=16), capi.RA_ERR_SHAPE, "divisible")
+    expect(ring(lib, dims(Sq=120, Sk=120), N=8, layout=2), capi.RA_ERR_SHAPE, "zigzag")
+    expect(ring(lib, dims(Sq=64), N=8), capi.RA_ERR_SHAPE, "Sq == Sk")
+    expect(ring(lib, dims(Sq=128), N=8, device=3), capi.RA_ERR_SHAPE, "S/N")
+    expect(ring(lib, dims(), causal=2), capi.RA_ERR_ENUM, "causal")
+    expect(ring(lib, dims(), out=None), capi.RA_ERR_NULL, "non-NULL")
+    need = lib.ra_ring_workspace_bytes(ctypes.byref(dims()), 8, 1, -1)
+    assert 0 < need < (1 << 40)
+    expect(ring(lib, dims(), layout=1), capi.RA_ERR_WORKSPACE, "required")
+    expect(ring(lib, dims(), layout=1, ws=FAKE, wsb=need - 1), capi.RA_ERR_WORKSPACE, "small")
+    expect(ring(lib, dims(), layout=2, ws=FAKE + 16, wsb=need), capi.RA_ERR_WORKSPACE, "256")
+
+
+def test_workspace_bytes(lib):
+    def ws(d, N, layout, device):
+        return lib.ra_ring_workspace_bytes(ctypes.byref(d), N, layout, device)
+
+    bad = ctypes.c_size_t(-1).value
+    assert ws(dims(Hq=3), 8, 0, -1) == bad and "multiple" in capi.last_error()
+    assert ws(dims(), 8, 0, -1) == 0 and capi.last_error() == ""
+    assert ws(dims(Sq=16), 8, 2, 0) == 0  # a device share needs no workspace
+    # 65536 tokens, 32/8 heads, D 128, bf16, striped: Q + out copies, K + V copies, lse copy
+    d = dims(Hq=32, Hkv=8, Sq=65536, Sk=65536)
+    q = 32 * 65536 * 128 * 2
+    kv = 8 * 65536 * 128 * 2
+    assert ws(d, 8, 1, -1) == 2 * q + 2 * kv + 32 * 65536 * 4
+
+
+def test_permute_and_positions_errors(lib):
+    P = lib.ra_permute
+    expect(P(None, FAKE, 1, 16, 256, 4, 0, 0, None), capi.RA_ERR_NULL, "src")
+    expect(P(FAKE, FAKE, 1, 16, 6, 4, 0, 0, None), capi.RA_ERR_SHAPE, "multiple of 4")
+    expect(P(FAKE, FAKE, 1, 16, 256, 4, 5, 0, None), capi.RA_ERR_ENUM, "layout")
+    expect(P(FAKE, FAKE, 1, 16, 256, 4, 1, 2, None), capi.RA_ERR_ENUM, "inverse")
+    expect(P(FAKE, FAKE, 1, 18, 256, 4, 1, 0, None), capi.RA_ERR_SHAPE, "divisible")
+    expect(P(FAKE, FAKE, 1, 12, 256, 4, 2, 0, None), capi.RA_ERR_SHAPE, "zigzag")
+    expect(P(FAKE + 4, FAKE, 1, 16, 256, 4, 1, 0, None), capi.RA_ERR_SHAPE, "misaligned")
+    Q = lib.ra_positions
+    expect(Q(None, 16, 4, 0, -1, None), capi.RA_ERR_NULL, "pos")
+    expect(Q(FAKE, 16, 4, 0, 4, None), capi.RA_ERR_ENUM, "device")
+    expect(Q(FAKE, 16, 4, 9, 0, None), capi.RA_ERR_ENUM, "layout")
+    expect(Q(FAKE, 15, 4, 0, 0, None), capi.RA_ERR_SHAPE, "divisible")
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 1, 8, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        capi.ra_ring(x, x, x, x, torch.zeros(1, 1, 8), 1)
