@@ -75,7 +75,27 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target oracle time for the CPU baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (contiguous ra_permute) so that "
+                         "HBM byte counters can be scaled against a kernel of known traffic")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """One contiguous-layout ra_permute over 1 GiB: reads 1 GiB and writes 1 GiB."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+
+    n = 1 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    rows = src.view(1, n // 256, 64)
+    for _ in range(3):
+        ra.ra_permute(rows, dst.view(1, n // 256, 64), 1, "contiguous")
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}), flush=True)
 
 
 def blas_threads():
@@ -106,7 +126,7 @@ def cpu_baseline(q, k, v, cfg, layout, device, seconds, gpu_out=None, gpu_lse=No
     errs = [0.0, 0.0]
     seed = 1000
     while t_used < seconds and rows_done < Sq * Hq:
-        sample = workloads.sample_rows(Hq, Sq, 32, seed)
+        sample = workloads.sample_rows(Hq, Sq, 1, seed)
         seed += 1
         rows = [(0, h, i) for (h, i) in sample]
         t0 = time.perf_counter()
@@ -148,6 +168,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(3)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     wkey, layout, device = WORKLOADS[args.workload]
     cfg = workloads.WORKLOADS[wkey]
     S, N, D, Hq, Hkv = cfg["S"], cfg["N"], cfg["D"], cfg["Hq"], cfg["Hkv"]

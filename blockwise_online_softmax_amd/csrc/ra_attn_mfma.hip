@@ -10,25 +10,34 @@
 // head) and walks the key/value blocks in ring order, 64 keys per tile; each
 // of its NW waves owns 32 query rows.  Per tile and wave:
 //   S^T[64 keys x 32 queries] = K_tile . Q^T   v_mfma_f32_32x32x16_bf16,
-//        A = K rows from LDS, B = Q^T fragments held in registers,
+//        A = K rows read from LDS, B = Q^T fragments held in registers;
 //   softmax on S^T: every lane holds 32 scores of ONE query (the other 32 of
 //        that query sit in lane ^ 32), so the row max needs one cross-lane
-//        exchange and the running state (m, l, o) is per lane,
+//        exchange and the running state (m, l, o) is per lane;
 //   O^T[D x 32 queries] += V^T . P^T   v_mfma_f32_32x32x16_bf16,
-//        A = V^T from LDS (V is transposed while it is written to LDS),
-//        B = P straight from the S^T accumulators rounded to bf16.  The key
-//        order inside the contraction is permuted to match the lane layout of
-//        S^T; V^T is read with the same permutation.
+//        A = V^T read from the row-major V tile with the LDS transpose read
+//        (ds_read_b64_tr_b16), B = P straight from the S^T accumulators
+//        rounded to bf16.  The key order inside the contraction follows the
+//        lane layout of S^T and the transpose reads use the same order.
 // Operands (32x32x16): lane l holds A[l%32][8*(l/32) .. +8] and
 // B[8*(l/32) .. +8][l%32]; accumulator element i of lane l is
 // C[8*(i/4) + 4*(l/32) + i%4][l%32].
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element
+// i%4 of the 8 bytes that lane 4e + i/4 addressed, as its element e.
+//
+// Tiles move HBM -> LDS without registers (global_load_lds, 16 bytes per
+// lane), double-buffered, one barrier per tile; the next tile's copy is in
+// flight while the current one is computed.  Both tiles are row-major with
+// the 16-byte units of a row XOR-swizzled (K by row, V by 2*row) so the MFMA
+// operand reads are free of bank conflicts; the swizzle is applied by choosing
+// which global unit each lane copies.
 //
 // Exponentials run in base 2 with scale*log2(e) folded into one FMA.  The
 // reference max used for the exponentials is only raised when the tile max
 // exceeds it by more than 2^8 (lazy rescale): the identity holds for any
 // reference value, p stays <= 256 (exact range for bf16 and fp32 sums), and
-// the 64-wide rescale of o is skipped for most tiles.  The exact running max
-// is tracked beside it and applied before the state leaves the kernel.
+// the rescale of o is skipped for most tiles.  The exact running max is
+// tracked beside it and applied before the state leaves the kernel.
 //
 // Causal masking on global positions (key visible iff pos_k <= pos_q).  With
 // device-ordered data (POS_ANALYTIC) positions are computed from the layout
@@ -36,11 +45,6 @@
 // tile's last position are skipped and tiles wholly before its first
 // position run without a mask.  With explicit position arrays (POS_ARRAY)
 // every tile is classified from the min/max of its key positions.
-//
-// K and V tiles are double-buffered in LDS (global -> registers -> LDS, one
-// barrier per tile); the next tile's global loads are in flight while the
-// current tile is computed.  LDS layouts are XOR-swizzled so that both the
-// writes and the MFMA operand reads are free of bank conflicts.
 #include "ra_internal.h"
 
 namespace ra {
@@ -52,8 +56,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((address_space(3))) char lds_t;
 
 constexpr int BN = 64;            // keys per tile
 constexpr float kLazy = 8.0f;     // log2 of the largest p admitted before rescaling
@@ -70,6 +76,25 @@ __device__ inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ inline u32x4 lds_read128(const lds_t* p) {
+  return *(const __attribute__((address_space(3))) u32x4*)p;
+}
+
+__device__ inline u32x2 lds_read_tr(const lds_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 16 bytes per lane, global -> LDS at dst + 16*lane (dst uniform).
+__device__ inline void dma16(const void* src, lds_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+__device__ inline void wait_dma() {
+  // vmcnt(0); expcnt and lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 __device__ inline int wave_min(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
@@ -83,16 +108,19 @@ __device__ inline int wave_max(int v) {
 
 // A key tile to process: keys [start, start + n) of the Sk_tot axis, from key
 // block j (local indices a0 .. a0+n-1); `full` = no element needs a mask.
+// POS_ANALYTIC: key kt of the tile has position (kt < split ? p0 : p1) +
+// kt * stride (layouts are piecewise linear in the local index).
+// POS_ARRAY: kp = this lane's key position (key start + lane).
 struct Tile {
   int64_t start;
-  int j, a0, n;
+  int n;
   bool full;
-  int kp;  // POS_ARRAY: this lane's key position (key start + lane), for masking
+  int p0, p1, split, stride;
+  int kp;
 };
 
-template <int D, int NW, bool CAUSAL, int POS>
+template <bool CAUSAL, int POS>
 struct TileWalker {
-  // uniform walk state
   int s, tt, j;
   bool bfull;
   int ntile_blk;
@@ -130,20 +158,31 @@ struct TileWalker {
       const int a0 = tt * BN;
       const int n = min(BN, P.klen - a0);
       T.start = (int64_t)j * P.klen + a0;
-      T.j = j;
-      T.a0 = a0;
       T.n = n;
       T.kp = 0;
       bool full = (n == BN);
-      if (CAUSAL && POS == POS_ANALYTIC && !bfull) {
+      if (CAUSAL && POS == POS_ANALYTIC) {
         const int kf = layout_pos(P.layout, P.N, P.blk, j, a0);
-        const int kl = layout_pos(P.layout, P.N, P.blk, j, a0 + n - 1);
-        if (kf > qmax) {  // positions ascend in a block: nothing after is visible
-          ++s;
-          tt = 0;
-          continue;
+        if (!bfull) {
+          const int kl = layout_pos(P.layout, P.N, P.blk, j, a0 + n - 1);
+          if (kf > qmax) {  // positions ascend in a block: nothing after is visible
+            ++s;
+            tt = 0;
+            continue;
+          }
+          full = full && (kl <= qmin);
         }
-        full = full && (kl <= qmin);
+        T.stride = P.layout == RA_STRIPED ? P.N : 1;
+        T.p0 = kf;
+        T.split = BN;
+        T.p1 = kf;
+        if (P.layout == RA_ZIGZAG) {
+          const int c = P.blk >> 1;
+          if (a0 < c && a0 + n > c) {
+            T.split = c - a0;
+            T.p1 = layout_pos(P.layout, P.N, P.blk, j, c) - (c - a0);
+          }
+        }
       }
       ++tt;
       if (CAUSAL && POS == POS_ARRAY) {
@@ -163,19 +202,18 @@ struct TileWalker {
 
 template <int D, int NW, bool CAUSAL, int POS, bool STATE_IO>
 __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
-  constexpr int NC = D / 16;     // 16-wide d chunks of the QK^T contraction
-  constexpr int NDB = D / 32;    // 32-row d blocks of O^T
-  constexpr int UNITS = D / 8;   // 16-byte units per K row
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32;
-  constexpr int KUNITS = BN * UNITS;           // 16-byte units per K tile
-  constexpr int KPER = (KUNITS + NT - 1) / NT;
-  constexpr int VTASKS = (BN / 4) * (D / 8);   // 4 keys x 8 d per task
-  constexpr int VPER = (VTASKS + NT - 1) / NT;
-  constexpr int KSW = UNITS < 16 ? UNITS - 1 : 15;  // K swizzle mask
+  constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
+  constexpr int NDB = D / 32;         // 32-row d blocks of O^T
+  constexpr int UNITS = D / 8;        // 16-byte units per row
+  constexpr int ROWB = D * 2;         // bytes per row
+  constexpr int TILE_BYTES = BN * ROWB;
+  constexpr int XPW = TILE_BYTES / 1024 / NW;  // 1 KB copies per wave per tensor
+  constexpr int KMASK = (UNITS < 16 ? UNITS : 16) - 1;
+  constexpr int VMASK = UNITS - 1;
+  static_assert(XPW * NW * 1024 == TILE_BYTES, "tile must split into 1 KB copies per wave");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * BN];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TILE_BYTES];
+  lds_t* smem = (lds_t*)smem_raw;  // generic -> LDS address space
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,8 +237,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   const int h = g * G + hg;
   const int dev = P.dev0 + qi;
 
-  const int a0q = t * BM;                       // first local row of the tile
-  const int nrows = min(BM, P.qlen - a0q);
+  const int a0q = t * (NW * 32);                // first local row of the tile
+  const int nrows = min(NW * 32, P.qlen - a0q);
   const int la = a0q + wave * 32 + r;           // this lane's local query row
   const bool rvalid = la < P.qlen;
   const int64_t qrow = (int64_t)qi * P.qlen + la;
@@ -267,91 +305,74 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
       }
   }
 
-  // ---- tile loaders ----
-  u32x4 kreg[KPER];
-  u32x4 vreg[VPER][4];
-  auto gload = [&](const Tile& T) {
+  // ---- per-lane LDS offsets of the MFMA operands (fixed for every tile) ----
+  int kofs[NC];  // K rows kb*32 + r, unit 2c + hi
 #pragma unroll
-    for (int e = 0; e < KPER; ++e) {
-      const int x = tid + e * NT;
-      const int key = x / UNITS, u = x % UNITS;
-      kreg[e] = (x < KUNITS && key < T.n)
-                    ? *reinterpret_cast<const u32x4*>(Kg + (T.start + key) * D + u * 8)
-                    : u32x4{0, 0, 0, 0};
+  for (int c = 0; c < NC; ++c) kofs[c] = r * ROWB + ((((2 * c + hi) ^ (r & KMASK))) << 4);
+  int vofs[NDB];  // transpose reads: key 4hi + (lane%16)/4, d 32db + 16((lane/16)%2) + 4(lane%4)
+  {
+    const int vkey = 4 * hi + ((lane & 15) >> 2);
+    const int sw = (2 * vkey) & VMASK;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int u = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      vofs[db] = vkey * ROWB + ((u ^ sw) << 4) + ((lane & 1) << 3);
     }
+  }
+
+  // ---- tile copy: HBM -> LDS, swizzled, rows past the tile end clamped ----
+  auto issue_tile = [&](const Tile& T, lds_t* kdst) {
+    lds_t* vdst = kdst + TILE_BYTES;
 #pragma unroll
-    for (int e = 0; e < VPER; ++e) {
-      const int y = tid + e * NT;
-      const int kq = y % 16, dq = y / 16;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = 4 * kq + rr;
-        vreg[e][rr] = (y < VTASKS && key < T.n)
-                          ? *reinterpret_cast<const u32x4*>(Vg + (T.start + key) * D + dq * 8)
-                          : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < KPER; ++e) {
-      const int x = tid + e * NT;
-      if (x < KUNITS) {
-        const int key = x / UNITS, u = x % UNITS;
-        *reinterpret_cast<u32x4*>(&Ks[buf][key * D + ((u ^ (key & KSW)) * 8)]) = kreg[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < VPER; ++e) {
-      const int y = tid + e * NT;
-      if (y < VTASKS) {
-        const int kq = y % 16, dq = y / 16;
-        const u32x4 r0 = vreg[e][0], r1 = vreg[e][1], r2 = vreg[e][2], r3 = vreg[e][3];
-#pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          // d = 8dq + 2wi (low halves) and 8dq + 2wi + 1 (high halves)
-          const u32x2 lo = {(r0[wi] & 0xffffu) | (r1[wi] << 16),
-                            (r2[wi] & 0xffffu) | (r3[wi] << 16)};
-          const u32x2 hv = {(r0[wi] >> 16) | (r1[wi] & 0xffff0000u),
-                            (r2[wi] >> 16) | (r3[wi] & 0xffff0000u)};
-          const int d0 = dq * 8 + 2 * wi, d1 = d0 + 1;
-          *reinterpret_cast<u32x2*>(&Vt[buf][d0 * BN + ((kq ^ (d0 & 15)) * 4)]) = lo;
-          *reinterpret_cast<u32x2*>(&Vt[buf][d1 * BN + ((kq ^ (d1 & 15)) * 4)]) = hv;
-        }
-      }
+    for (int i = 0; i < XPW; ++i) {
+      const int x = wave + NW * i;
+      const int U = x * 64 + lane;
+      const int row = U / UNITS;
+      const int ph = U % UNITS;
+      const int64_t grow = T.start + min(row, T.n - 1);
+      dma16(Kg + grow * D + ((ph ^ (row & KMASK)) << 3), kdst + x * 1024);
+      dma16(Vg + grow * D + ((ph ^ ((2 * row) & VMASK)) << 3), vdst + x * 1024);
     }
   };
 
-  TileWalker<D, NW, CAUSAL, POS> walker;
+  TileWalker<CAUSAL, POS> walker;
   walker.init(P);
   Tile cur;
   bool have = walker.next(P, dev, qmin, qmax, cur);
-  if (have) {
-    gload(cur);
-    lstore(0);
-  }
+  if (have) issue_tile(cur, smem);
+  wait_dma();
   __syncthreads();
   int buf = 0;
 
-  while (have) {
-    Tile nxt;
-    const bool have_next = walker.next(P, dev, qmin, qmax, nxt);
-    if (have_next) gload(nxt);
-
-    // ---- S^T = K . Q^T (two 32-key blocks) ----
+  // One tile: copy the next tile into `nb` while computing on `cb`.  The two
+  // restrict-qualified buffers tell the compiler the copy cannot alias the
+  // operand reads, so no wait for the copy is placed before them.
+  auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& nt,
+                  bool have_next) {
+    if (have_next) issue_tile(nt, nb);
+    const lds_t* Kb = cb;
+    const lds_t* Vb = cb + TILE_BYTES;
+    // ---- S^T = K . Q^T (two 32-key blocks); operand reads run one step
+    //      ahead of the MFMAs that consume them ----
     f32x16 sacc[2];
+    {
+      u32x4 ka[2][2];
+      ka[0][0] = lds_read128(Kb + kofs[0]);
+      ka[0][1] = lds_read128(Kb + kofs[0] + 32 * ROWB);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = kb * 32 + r;
-        const int u = 2 * c + hi;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[buf][key * D + ((u ^ (key & KSW)) * 8)]);
-        sacc[kb] = mfma(a, qf[c], sacc[kb]);
+      for (int c = 0; c < NC; ++c) {
+        if (c + 1 < NC) {
+          ka[(c + 1) & 1][0] = lds_read128(Kb + kofs[c + 1]);
+          ka[(c + 1) & 1][1] = lds_read128(Kb + kofs[c + 1] + 32 * ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (c == 0) {
+          sacc[0] = mfma(ka[0][0], qf[0], f32x16{});
+          sacc[1] = mfma(ka[0][1], qf[0], f32x16{});
+        } else {
+          sacc[0] = mfma(ka[c & 1][0], qf[c], sacc[0]);
+          sacc[1] = mfma(ka[c & 1][1], qf[c], sacc[1]);
+        }
       }
     }
 
@@ -366,12 +387,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
           if (CAUSAL) {
             int kp;
             if (POS == POS_ANALYTIC)
-              kp = layout_pos(P.layout, P.N, P.blk, cur.j, cur.a0 + kt);
+              kp = (kt < cur.split ? cur.p0 : cur.p1) + kt * cur.stride;
             else
               kp = __shfl(cur.kp, kt);
             vis = vis && (kp <= qpos);
           }
-          if (!vis) sacc[kb][i] = -__builtin_inff();
+          sacc[kb][i] = vis ? sacc[kb][i] : -__builtin_inff();
         }
     }
 
@@ -410,23 +431,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
                            pack2(pv[8 * hh + 4], pv[8 * hh + 5]), pack2(pv[8 * hh + 6], pv[8 * hh + 7])};
     }
 
-    // ---- O^T += V^T . P^T ----
+    // ---- O^T += V^T . P^T; transpose reads one MFMA ahead ----
+    {
+      constexpr int NSTEP = 4 * NDB;  // (kb, half) x d blocks
+      u32x4 va[2];
+      auto vread = [&](int st) {
+        const int kh = st / NDB, db = st % NDB;  // kh = 2*kb + half
+        const lds_t* vp = Vb + vofs[db] + (16 * kh) * ROWB;
+        const u32x2 x0 = lds_read_tr(vp);
+        const u32x2 x1 = lds_read_tr(vp + 8 * ROWB);
+        return u32x4{x0.x, x0.y, x1.x, x1.y};
+      };
+      va[0] = vread(0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int e8 = 8 * kb + 4 * hh + hi;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = db * 32 + r;
-          const uint16_t* row = &Vt[buf][d * BN];
-          const u32x2 x0 = *reinterpret_cast<const u32x2*>(row + ((e8 ^ (d & 15)) * 4));
-          const u32x2 x1 = *reinterpret_cast<const u32x2*>(row + (((e8 + 2) ^ (d & 15)) * 4));
-          o[db] = mfma(u32x4{x0.x, x0.y, x1.x, x1.y}, pf[kb][hh], o[db]);
-        }
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + 1 < NSTEP) va[(st + 1) & 1] = vread(st + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kh = st / NDB, db = st % NDB;
+        o[db] = mfma(va[st & 1], pf[kh >> 1][kh & 1], o[db]);
       }
+    }
+  };
 
-    if (have_next) lstore(buf ^ 1);
+  while (have) {
+    Tile nxt;
+    const bool have_next = walker.next(P, dev, qmin, qmax, nxt);
+    if (buf == 0)
+      tile(smem, smem + 2 * TILE_BYTES, nxt, have_next);
+    else
+      tile(smem + 2 * TILE_BYTES, smem, nxt, have_next);
+    wait_dma();
     __syncthreads();
     buf ^= 1;
     cur = nxt;

@@ -16,17 +16,22 @@ Workloads (sizes from the pages' cases and a Llama-3-8B attention layer:
   share1m   one device's zigzag share of S = 1,048,576 over N = 8: 131072
             queries (device 0) against all 8 K/V blocks in device order,
             causal, 32/8 heads, bf16.
-Every bf16 tensor is drawn as torch.randn in float32 from a CPU
-torch.Generator seeded with the workload's seed (Q, then K, then V), then
-rounded to bf16 (round-to-nearest-even).  Large tensors are drawn in chunks
-of CHUNK_ROWS rows along the flattened [rows, D] view, in order, from the same
-generator, so the draw is deterministic for a given seed and shape.
+Every bf16 tensor of the large workloads is drawn as N(0,1) float32 with
+numpy and rounded to bf16 (round-to-nearest-even): tensor t (0 = Q, 1 = K,
+2 = V) of a workload with seed s uses numpy.random.SeedSequence([s, t]); its
+flattened elements are cut into chunks of CHUNK elements, chunk c is filled
+by Generator(PCG64(child c of that sequence)).standard_normal(float32).  The
+draw is deterministic for any number of worker threads.
 """
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
 
-CHUNK_ROWS = 1 << 16
+CHUNK = 1 << 22
+THREADS = min(16, os.cpu_count() or 1)
 
 WORKLOADS = {
     "tiny": dict(B=1, Hq=1, Hkv=1, S=12, N=4, D=8, dtype="f32", causal=False,
@@ -50,25 +55,29 @@ def tiny_inputs():
     return Q, K, V
 
 
-def randn(shape, gen, dtype=torch.bfloat16):
-    """N(0,1) draw in float32 from `gen`, chunked by rows, rounded to `dtype`."""
-    shape = tuple(int(s) for s in shape)
-    D = shape[-1]
-    rows = int(np.prod(shape[:-1]))
-    out = torch.empty((rows, D), dtype=dtype)
-    for r0 in range(0, rows, CHUNK_ROWS):
-        r1 = min(rows, r0 + CHUNK_ROWS)
-        out[r0:r1] = torch.randn((r1 - r0, D), generator=gen, dtype=torch.float32).to(dtype)
+def randn(shape, seed, index, dtype=torch.bfloat16):
+    """N(0,1) tensor of `shape`: float32 chunks from spawned PCG64 streams, rounded to dtype."""
+    shape = tuple(int(x) for x in shape)
+    n = int(np.prod(shape))
+    nchunks = (n + CHUNK - 1) // CHUNK
+    kids = np.random.SeedSequence([int(seed), int(index)]).spawn(nchunks)
+    out = torch.empty(n, dtype=dtype)
+
+    def fill(c):
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        x = np.random.Generator(np.random.PCG64(kids[c])).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi].copy_(torch.from_numpy(x))
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(fill, range(nchunks)))
     return out.view(shape)
 
 
 def qkv(B, Hq, Hkv, Sq, Sk, D, seed, dtype=torch.bfloat16):
-    """Q [B,Hq,Sq,D], K, V [B,Hkv,Sk,D] on the CPU, drawn in that order."""
-    gen = torch.Generator(device="cpu")
-    gen.manual_seed(int(seed))
-    q = randn((B, Hq, Sq, D), gen, dtype)
-    k = randn((B, Hkv, Sk, D), gen, dtype)
-    v = randn((B, Hkv, Sk, D), gen, dtype)
+    """Q [B,Hq,Sq,D], K, V [B,Hkv,Sk,D] on the CPU (tensor indices 0, 1, 2)."""
+    q = randn((B, Hq, Sq, D), seed, 0, dtype)
+    k = randn((B, Hkv, Sk, D), seed, 1, dtype)
+    v = randn((B, Hkv, Sk, D), seed, 2, dtype)
     return q, k, v
 
 
@@ -88,20 +97,23 @@ def workload_inputs(name):
     return qkv(w["B"], w["Hq"], w["Hkv"], Sq, w["S"], w["D"], w["seed"])
 
 
-def sample_rows(Hq, Sq, n_rows, seed, must_include=()):
-    """Seeded (h, i) row sample: n_rows // Hq rows per head plus `must_include`.
+def sample_rows(Hq, Sq, per_head, seed, strata=None, include_ends=False):
+    """Seeded sample of (h, i) query rows: `per_head` rows for every head.
 
-    must_include: sequence indices every head includes (chunk first/last rows).
-    Returns a sorted list of (h, i).
+    strata: index ranges (lo, hi) that share a head's rows equally (default
+    the whole range); include_ends makes every stratum contribute its first
+    and last index.  Returns a list of (h, i) sorted by head, then index.
     """
     rng = np.random.default_rng(seed)
-    per_head = max(1, n_rows // Hq)
+    strata = strata or [(0, Sq)]
+    share = max(1, per_head // len(strata))
     rows = []
     for h in range(Hq):
-        fixed = sorted(set(int(i) for i in must_include))
-        rest = per_head - len(fixed)
-        pool = np.setdiff1d(np.arange(Sq), np.array(fixed, dtype=np.int64))
-        pick = rng.choice(pool, size=max(0, rest), replace=False) if rest > 0 else []
-        for i in sorted(fixed + [int(x) for x in pick])[:per_head]:
-            rows.append((h, i))
+        picks = set()
+        for lo, hi in strata:
+            fixed = {lo, hi - 1} if include_ends else set()
+            pool = np.setdiff1d(np.arange(lo, hi), np.array(sorted(fixed), dtype=np.int64))
+            extra = rng.choice(pool, size=max(0, share - len(fixed)), replace=False)
+            picks |= fixed | set(int(x) for x in extra)
+        rows += [(h, i) for i in sorted(picks)]
     return rows
