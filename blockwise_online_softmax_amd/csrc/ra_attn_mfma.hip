@@ -305,33 +305,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
       }
   }
 
-  // ---- per-lane LDS offsets of the MFMA operands (fixed for every tile) ----
-  int kofs[NC];  // K rows kb*32 + r, unit 2c + hi
-#pragma unroll
-  for (int c = 0; c < NC; ++c) kofs[c] = r * ROWB + ((((2 * c + hi) ^ (r & KMASK))) << 4);
-  int vofs[NDB];  // transpose reads: key 4hi + (lane%16)/4, d 32db + 16((lane/16)%2) + 4(lane%4)
+  // ---- per-lane LDS offsets of the MFMA operands (fixed for every tile).
+  // The swizzle is a XOR of 16-byte unit indices and the unit index of chunk
+  // c (K) or d block db (V) only adds bits above the lane's own, so every
+  // offset is the lane's first offset XOR a constant. ----
+  // K: row kb*32 + r, unit 2c + hi        -> kofs0 ^ (c << 5)
+  const int kofs0 = r * ROWB + ((hi ^ (r & KMASK)) << 4);
+  // V^T (transpose reads): key 4hi + (lane%16)/4, d 32db + 16((lane/16)%2) + 4(lane%4)
+  //                                       -> vofs0 ^ (db << 6)
+  int vofs0;
   {
     const int vkey = 4 * hi + ((lane & 15) >> 2);
-    const int sw = (2 * vkey) & VMASK;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int u = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      vofs[db] = vkey * ROWB + ((u ^ sw) << 4) + ((lane & 1) << 3);
-    }
+    const int u = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    vofs0 = vkey * ROWB + ((u ^ ((2 * vkey) & VMASK)) << 4) + ((lane & 1) << 3);
   }
 
-  // ---- tile copy: HBM -> LDS, swizzled, rows past the tile end clamped ----
+  // ---- tile copy: HBM -> LDS, swizzled, rows past the tile end clamped;
+  //      uniform tile base + 32-bit lane offset ----
   auto issue_tile = [&](const Tile& T, lds_t* kdst) {
     lds_t* vdst = kdst + TILE_BYTES;
+    const char* kb = reinterpret_cast<const char*>(Kg + T.start * D);
+    const char* vb = reinterpret_cast<const char*>(Vg + T.start * D);
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
       const int x = wave + NW * i;
       const int U = x * 64 + lane;
       const int row = U / UNITS;
       const int ph = U % UNITS;
-      const int64_t grow = T.start + min(row, T.n - 1);
-      dma16(Kg + grow * D + ((ph ^ (row & KMASK)) << 3), kdst + x * 1024);
-      dma16(Vg + grow * D + ((ph ^ ((2 * row) & VMASK)) << 3), vdst + x * 1024);
+      const int rb = min(row, T.n - 1) * ROWB;
+      dma16(kb + rb + ((ph ^ (row & KMASK)) << 4), kdst + x * 1024);
+      dma16(vb + rb + ((ph ^ ((2 * row) & VMASK)) << 4), vdst + x * 1024);
     }
   };
 
@@ -344,111 +347,162 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   __syncthreads();
   int buf = 0;
 
-  // One tile: copy the next tile into `nb` while computing on `cb`.  The two
-  // restrict-qualified buffers tell the compiler the copy cannot alias the
-  // operand reads, so no wait for the copy is placed before them.
-  auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& nt,
-                  bool have_next) {
-    if (have_next) issue_tile(nt, nb);
-    const lds_t* Kb = cb;
-    const lds_t* Vb = cb + TILE_BYTES;
-    // ---- S^T = K . Q^T (two 32-key blocks); operand reads run one step
-    //      ahead of the MFMAs that consume them ----
-    f32x16 sacc[2];
-    {
-      u32x4 ka[2][2];
-      ka[0][0] = lds_read128(Kb + kofs[0]);
-      ka[0][1] = lds_read128(Kb + kofs[0] + 32 * ROWB);
+  // Causal / ragged mask of one 32-key half (partial tiles only).
+  auto mask_half = [&](f32x16& sa, int kb, const Tile& T) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) {
-          ka[(c + 1) & 1][0] = lds_read128(Kb + kofs[c + 1]);
-          ka[(c + 1) & 1][1] = lds_read128(Kb + kofs[c + 1] + 32 * ROWB);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (c == 0) {
-          sacc[0] = mfma(ka[0][0], qf[0], f32x16{});
-          sacc[1] = mfma(ka[0][1], qf[0], f32x16{});
-        } else {
-          sacc[0] = mfma(ka[c & 1][0], qf[c], sacc[0]);
-          sacc[1] = mfma(ka[c & 1][1], qf[c], sacc[1]);
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int kt = kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
+      bool vis = kt < T.n;
+      if (CAUSAL) {
+        int kp;
+        if (POS == POS_ANALYTIC)
+          kp = (kt < T.split ? T.p0 : T.p1) + kt * T.stride;
+        else
+          kp = __shfl(T.kp, kt);
+        vis = vis && (kp <= qpos);
       }
+      sa[i] = vis ? sa[i] : -__builtin_inff();
     }
+  };
 
-    // ---- mask (partial tiles only) ----
-    if (!cur.full) {
+  // Online softmax of one 32-key half (base 2, lazy rescale).  Updates m2,
+  // mtrue and lsum, writes the half's bf16 P and returns the factor that o
+  // must be multiplied by (applied by the caller, after the MFMAs that still
+  // accumulate into o under the old reference).
+  auto softmax_half = [&](const f32x16& sa, u32x4& pf0, u32x4& pf1, bool& anyneed) {
+    float tmax = sa[0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kt = kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-          bool vis = kt < cur.n;
-          if (CAUSAL) {
-            int kp;
-            if (POS == POS_ANALYTIC)
-              kp = (kt < cur.split ? cur.p0 : cur.p1) + kt * cur.stride;
-            else
-              kp = __shfl(cur.kp, kt);
-            vis = vis && (kp <= qpos);
-          }
-          sacc[kb][i] = vis ? sacc[kb][i] : -__builtin_inff();
-        }
+    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sa[i]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                       false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lane and lane^32
     }
-
-    // ---- online softmax (base 2, lazy rescale) ----
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float tm2 = tmax * P.sl2;
     mtrue = fmaxf(mtrue, tm2);
     const bool need = tm2 > m2 + kLazy;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m2 - tm2) : 1.0f;
-      m2 = need ? tm2 : m2;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
+    const float mnew = need ? tm2 : m2;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.0f;
+    m2 = mnew;
+    anyneed = __any(need);
     const float msub = m2 > -__builtin_inff() ? m2 : 0.f;
-    u32x4 pf[2][2];  // bf16 P for the four PV contractions (kb, half)
+    float pv[16];
+    float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], P.sl2, -msub));
-        lsum += pv[i];
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        pf[kb][hh] = u32x4{pack2(pv[8 * hh + 0], pv[8 * hh + 1]), pack2(pv[8 * hh + 2], pv[8 * hh + 3]),
-                           pack2(pv[8 * hh + 4], pv[8 * hh + 5]), pack2(pv[8 * hh + 6], pv[8 * hh + 7])};
+    for (int i = 0; i < 16; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], P.sl2, -msub));
+      ps += pv[i];
     }
+    lsum = lsum * alpha + ps;
+    pf0 = u32x4{pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7])};
+    pf1 = u32x4{pack2(pv[8], pv[9]), pack2(pv[10], pv[11]), pack2(pv[12], pv[13]),
+                pack2(pv[14], pv[15])};
+    return alpha;
+  };
 
-    // ---- O^T += V^T . P^T; transpose reads one MFMA ahead ----
+  // Keeps a softmax result in the scheduling region where it is written (an
+  // empty asm that reads it), so the compiler cannot sink the exponentials
+  // below the branches that follow and lose their overlap with the MFMAs.
+  auto pin = [](const u32x4& a, const u32x4& b, float c) {
+    asm volatile("" ::"v"(a), "v"(b), "v"(c));
+  };
+
+  auto rescale_o = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+  };
+
+  // One tile: copy the next tile into `nb` while computing on `cb`.  The two
+  // restrict-qualified buffers tell the compiler the copy cannot alias the
+  // operand reads, so no wait for the copy is placed before them.
+  // Schedule per wave (MFMA and VALU of one wave overlap in hardware):
+  //   S0 = K[0:32] . Q^T              | next tile's copy issue
+  //   S1 = K[32:64] . Q^T             | softmax(S0)
+  //   O^T += V[0:32]^T . P0^T         | softmax(S1)
+  //   O^T += V[32:64]^T . P1^T
+  auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& ct,
+                  const Tile& nt, bool have_next) {
+    const lds_t* Kb = cb;
+    const lds_t* Vb = cb + TILE_BYTES;
+
+    // S0, with the copy of the next tile issued between the MFMAs
+    f32x16 s0, s1;
     {
-      constexpr int NSTEP = 4 * NDB;  // (kb, half) x d blocks
+      u32x4 ka[2];
+      ka[0] = lds_read128(Kb + kofs0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + 1 < NC) ka[(c + 1) & 1] = lds_read128(Kb + (kofs0 ^ ((c + 1) << 5)));
+        s0 = mfma(ka[c & 1], qf[c], c == 0 ? f32x16{} : s0);
+      }
+      issue_tile(have_next ? nt : ct, nb);  // the last tile re-copies itself: no branch
+    }
+    if (!ct.full) mask_half(s0, 0, ct);
+
+    // S1 | softmax(S0)
+    u32x4 pf[2][2];
+    bool need0, need1;
+    float alpha0, alpha1;
+    {
+      u32x4 ka[2];
+      ka[0] = lds_read128(Kb + kofs0 + 32 * ROWB);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + 1 < NC) ka[(c + 1) & 1] = lds_read128(Kb + (kofs0 ^ ((c + 1) << 5)) + 32 * ROWB);
+        s1 = mfma(ka[c & 1], qf[c], c == 0 ? f32x16{} : s1);
+      }
+      alpha0 = softmax_half(s0, pf[0][0], pf[0][1], need0);
+      pin(pf[0][0], pf[0][1], alpha0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // 10 VALU
+      }
+    }
+    if (need0) rescale_o(alpha0);
+    if (!ct.full) mask_half(s1, 1, ct);
+
+    constexpr int NSTEP = 2 * NDB;  // (half, d block) steps per 32 keys
+    auto vread = [&](int kb, int st) {
+      const int hh = st / NDB, db = st % NDB;
+      const lds_t* vp = Vb + (vofs0 ^ (db << 6)) + (32 * kb + 16 * hh) * ROWB;
+      const u32x2 x0 = lds_read_tr(vp);
+      const u32x2 x1 = lds_read_tr(vp + 8 * ROWB);
+      return u32x4{x0.x, x0.y, x1.x, x1.y};
+    };
+    // PV0 | softmax(S1)
+    {
       u32x4 va[2];
-      auto vread = [&](int st) {
-        const int kh = st / NDB, db = st % NDB;  // kh = 2*kb + half
-        const lds_t* vp = Vb + vofs[db] + (16 * kh) * ROWB;
-        const u32x2 x0 = lds_read_tr(vp);
-        const u32x2 x1 = lds_read_tr(vp + 8 * ROWB);
-        return u32x4{x0.x, x0.y, x1.x, x1.y};
-      };
-      va[0] = vread(0);
+      va[0] = vread(0, 0);
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) {
-        if (st + 1 < NSTEP) va[(st + 1) & 1] = vread(st + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        const int kh = st / NDB, db = st % NDB;
-        o[db] = mfma(va[st & 1], pf[kh >> 1][kh & 1], o[db]);
+        if (st + 1 < NSTEP) va[(st + 1) & 1] = vread(0, st + 1);
+        const int hh = st / NDB, db = st % NDB;
+        o[db] = mfma(va[st & 1], pf[0][hh], o[db]);
+      }
+      alpha1 = softmax_half(s1, pf[1][0], pf[1][1], need1);
+      pin(pf[1][0], pf[1][1], alpha1);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // 10 VALU
+      }
+    }
+    if (need1) rescale_o(alpha1);
+
+    // PV1
+    {
+      u32x4 va[2];
+      va[0] = vread(1, 0);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + 1 < NSTEP) va[(st + 1) & 1] = vread(1, st + 1);
+        const int hh = st / NDB, db = st % NDB;
+        o[db] = mfma(va[st & 1], pf[1][hh], o[db]);
       }
     }
   };
@@ -456,10 +510,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   while (have) {
     Tile nxt;
     const bool have_next = walker.next(P, dev, qmin, qmax, nxt);
-    if (buf == 0)
-      tile(smem, smem + 2 * TILE_BYTES, nxt, have_next);
-    else
-      tile(smem + 2 * TILE_BYTES, smem, nxt, have_next);
+    tile(smem + buf * (2 * TILE_BYTES), smem + (buf ^ 1) * (2 * TILE_BYTES), cur, nxt, have_next);
     wait_dma();
     __syncthreads();
     buf ^= 1;
@@ -477,7 +528,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
       for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     m2 = mtrue;
   }
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  float ltot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                     false, false);
+    ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // lane + lane^32
+  }
   if (!rvalid) return;
   if (STATE_IO) {
     if (hi == 0) {
