@@ -98,6 +98,24 @@ def copy_calibration():
                       "launches": 3}), flush=True)
 
 
+def recorded_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    record (profiles/attn_mfma_<workload>_traffic.json), or None when there is
+    no record or the kernel source changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(HERE, "profiles", f"attn_mfma_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(HERE, rec["kernel_source"]), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if sha != rec["kernel_source_sha256"]:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -241,7 +259,8 @@ def main():
         "algorithmic_tflop": round(flops / 1e12, 4),
         "roofline": {
             "bound": "mfma", "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": recorded_traffic(args.workload),
             "kernel_ms": round(kern_ms, 4),
         },
         "cpu_baseline": cpu,

@@ -59,7 +59,8 @@ def load(path=None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    # RA_LIB selects another build of the same library (A/B timing of variants)
+    p = path or os.environ.get("RA_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(
             f"{p} not found: build the HIP library first "

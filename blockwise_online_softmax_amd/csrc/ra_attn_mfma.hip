@@ -28,7 +28,7 @@
 // Tiles move HBM -> LDS without registers (global_load_lds, 16 bytes per
 // lane), double-buffered, one barrier per tile; the next tile's copy is in
 // flight while the current one is computed.  Both tiles are row-major with
-// the 16-byte units of a row XOR-swizzled (K by row, V by 2*row) so the MFMA
+// the 16-byte units of a row XOR-swizzled (K by row, V by 4*(row bits)) so the MFMA
 // operand reads are free of bank conflicts; the swizzle is applied by choosing
 // which global unit each lane copies.
 //
@@ -209,7 +209,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   constexpr int TILE_BYTES = BN * ROWB;
   constexpr int XPW = TILE_BYTES / 1024 / NW;  // 1 KB copies per wave per tensor
   constexpr int KMASK = (UNITS < 16 ? UNITS : 16) - 1;
-  constexpr int VMASK = UNITS - 1;
+  // V tile swizzle: a transpose read serves 32 lanes per cycle, which read 4
+  // key rows x 4 units; XOR by 4 * (row bits) spreads them over all banks.
+  constexpr auto vswz = [](int row) -> int {
+    return UNITS >= 16 ? 4 * (row & 3) : (UNITS == 8 ? 4 * ((row >> 1) & 1) : 0);
+  };
   static_assert(XPW * NW * 1024 == TILE_BYTES, "tile must split into 1 KB copies per wave");
 
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TILE_BYTES];
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   {
     const int vkey = 4 * hi + ((lane & 15) >> 2);
     const int u = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    vofs0 = vkey * ROWB + ((u ^ ((2 * vkey) & VMASK)) << 4) + ((lane & 1) << 3);
+    vofs0 = vkey * ROWB + ((u ^ vswz(vkey)) << 4) + ((lane & 1) << 3);
   }
 
   // ---- tile copy: HBM -> LDS, swizzled, rows past the tile end clamped;
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
       const int ph = U % UNITS;
       const int rb = min(row, T.n - 1) * ROWB;
       dma16(kb + rb + ((ph ^ (row & KMASK)) << 4), kdst + x * 1024);
-      dma16(vb + rb + ((ph ^ ((2 * row) & VMASK)) << 4), vdst + x * 1024);
+      dma16(vb + rb + ((ph ^ vswz(row)) << 4), vdst + x * 1024);
     }
   };
 
