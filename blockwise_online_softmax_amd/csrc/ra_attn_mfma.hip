@@ -369,14 +369,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     }
   };
 
-  // Online softmax of one 32-key half (base 2, lazy rescale).  Updates m2,
-  // mtrue and lsum, writes the half's bf16 P and returns the factor that o
-  // must be multiplied by (applied by the caller, after the MFMAs that still
-  // accumulate into o under the old reference).
-  auto softmax_half = [&](const f32x16& sa, u32x4& pf0, u32x4& pf1, bool& anyneed) {
-    float tmax = sa[0];
+  // ---- online softmax of one 32-key half, split so that its pieces can be
+  //      placed between MFMAs (base 2, lazy rescale) ----
+  // Part 1 (row max and the rescale decision): updates m2 and mtrue; returns
+  // the factor for o and l, and the reference subtracted in the exponentials.
+  struct Ref {
+    float alpha, msub;
+    bool any;
+  };
+  auto softmax_max = [&](const f32x16& sa) {
+    float tmax = fmaxf(fmaxf(sa[0], sa[1]), sa[2]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sa[i]);
+    for (int i = 3; i < 16; ++i) tmax = fmaxf(tmax, sa[i]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
                                                        false, false);
@@ -386,29 +390,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     mtrue = fmaxf(mtrue, tm2);
     const bool need = tm2 > m2 + kLazy;
     const float mnew = need ? tm2 : m2;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.0f;
+    Ref R;
+    R.alpha = need ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.0f;
     m2 = mnew;
-    anyneed = __any(need);
-    const float msub = m2 > -__builtin_inff() ? m2 : 0.f;
-    float pv[16];
-    float ps = 0.f;
+    R.any = __any(need);
+    R.msub = m2 > -__builtin_inff() ? m2 : 0.f;
+    return R;
+  };
+  // Part 2: exponentials of elements [e0, e1) of the half into pv, summed into ps.
+  auto softmax_exp = [&](const f32x16& sa, float msub, float* pv, float& ps, int e0, int e1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], P.sl2, -msub));
-      ps += pv[i];
+    for (int e = e0; e < e1; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], P.sl2, -msub));
+      ps += pv[e];
     }
-    lsum = lsum * alpha + ps;
+  };
+  auto pack_half = [&](const float* pv, u32x4& pf0, u32x4& pf1) {
     pf0 = u32x4{pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7])};
     pf1 = u32x4{pack2(pv[8], pv[9]), pack2(pv[10], pv[11]), pack2(pv[12], pv[13]),
                 pack2(pv[14], pv[15])};
-    return alpha;
   };
 
-  // Keeps a softmax result in the scheduling region where it is written (an
-  // empty asm that reads it), so the compiler cannot sink the exponentials
-  // below the branches that follow and lose their overlap with the MFMAs.
-  auto pin = [](const u32x4& a, const u32x4& b, float c) {
-    asm volatile("" ::"v"(a), "v"(b), "v"(c));
+  // Keeps a softmax result in the region where it is written (an empty asm
+  // that reads it), so the compiler cannot sink the exponentials below the
+  // branches that follow and lose their overlap with the MFMAs.
+  auto pin = [](const u32x4& a, const u32x4& c, float x) {
+    asm volatile("" ::"v"(a), "v"(c), "v"(x));
   };
 
   auto rescale_o = [&](float alpha) {
@@ -421,55 +428,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   // One tile: copy the next tile into `nb` while computing on `cb`.  The two
   // restrict-qualified buffers tell the compiler the copy cannot alias the
   // operand reads, so no wait for the copy is placed before them.
-  // Schedule per wave (MFMA and VALU of one wave overlap in hardware):
-  //   S0 = K[0:32] . Q^T              | next tile's copy issue
-  //   S1 = K[32:64] . Q^T             | softmax(S0)
-  //   O^T += V[0:32]^T . P0^T         | softmax(S1)
+  // Program order per wave (MFMA and VALU of one wave overlap in hardware;
+  // every LDS operand read is issued two MFMAs before its use; the fences
+  // keep the compiler from reordering across these points):
+  //   S0 = K[0:32] . Q^T            | next tile's copy issue
+  //   S1 = K[32:64] . Q^T           | softmax(S0) in 6 pieces
+  //   O^T += V[0:32]^T . P0^T       | softmax(S1) in 6 pieces
   //   O^T += V[32:64]^T . P1^T
+  constexpr int PD = 2;  // operand read distance, in MFMAs
   auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& ct,
                   const Tile& nt, bool have_next) {
     const lds_t* Kb = cb;
     const lds_t* Vb = cb + TILE_BYTES;
-
-    // S0, with the copy of the next tile issued between the MFMAs
-    f32x16 s0, s1;
-    {
-      u32x4 ka[2];
-      ka[0] = lds_read128(Kb + kofs0);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) ka[(c + 1) & 1] = lds_read128(Kb + (kofs0 ^ ((c + 1) << 5)));
-        s0 = mfma(ka[c & 1], qf[c], c == 0 ? f32x16{} : s0);
-      }
-      issue_tile(have_next ? nt : ct, nb);  // the last tile re-copies itself: no branch
-    }
-    if (!ct.full) mask_half(s0, 0, ct);
-
-    // S1 | softmax(S0)
-    u32x4 pf[2][2];
-    bool need0, need1;
-    float alpha0, alpha1;
-    {
-      u32x4 ka[2];
-      ka[0] = lds_read128(Kb + kofs0 + 32 * ROWB);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) ka[(c + 1) & 1] = lds_read128(Kb + (kofs0 ^ ((c + 1) << 5)) + 32 * ROWB);
-        s1 = mfma(ka[c & 1], qf[c], c == 0 ? f32x16{} : s1);
-      }
-      alpha0 = softmax_half(s0, pf[0][0], pf[0][1], need0);
-      pin(pf[0][0], pf[0][1], alpha0);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // 10 VALU
-      }
-    }
-    if (need0) rescale_o(alpha0);
-    if (!ct.full) mask_half(s1, 1, ct);
-
-    constexpr int NSTEP = 2 * NDB;  // (half, d block) steps per 32 keys
+    auto kread = [&](int kb, int c) {
+      return lds_read128(Kb + (kofs0 ^ (c << 5)) + kb * 32 * ROWB);
+    };
+    constexpr int NSTEP = 2 * NDB;  // (half, d block) PV steps per 32 keys
     auto vread = [&](int kb, int st) {
       const int hh = st / NDB, db = st % NDB;
       const lds_t* vp = Vb + (vofs0 ^ (db << 6)) + (32 * kb + 16 * hh) * ROWB;
@@ -477,36 +451,86 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
       const u32x2 x1 = lds_read_tr(vp + 8 * ROWB);
       return u32x4{x0.x, x0.y, x1.x, x1.y};
     };
-    // PV0 | softmax(S1)
+
+    // ---- S0, the next tile's copy issued halfway ----
+    f32x16 s0, s1;
     {
-      u32x4 va[2];
-      va[0] = vread(0, 0);
+      u32x4 ka[PD + 1];
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        if (st + 1 < NSTEP) va[(st + 1) & 1] = vread(0, st + 1);
-        const int hh = st / NDB, db = st % NDB;
-        o[db] = mfma(va[st & 1], pf[0][hh], o[db]);
-      }
-      alpha1 = softmax_half(s1, pf[1][0], pf[1][1], need1);
-      pin(pf[1][0], pf[1][1], alpha1);
+      for (int c = 0; c < PD; ++c) ka[c] = kread(0, c);
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // 10 VALU
+      for (int c = 0; c < NC; ++c) {
+        if (c + PD < NC) ka[(c + PD) % (PD + 1)] = kread(0, c + PD);
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = mfma(ka[c % (PD + 1)], qf[c], c == 0 ? f32x16{} : s0);
+        if (c == NC / 2) issue_tile(have_next ? nt : ct, nb);  // last tile re-copies itself
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (need1) rescale_o(alpha1);
+    if (!ct.full) mask_half(s0, 0, ct);
 
-    // PV1
+    // ---- S1 | softmax(S0) ----
+    u32x4 pf[2][2];
+    Ref R0, R1;
     {
-      u32x4 va[2];
-      va[0] = vread(1, 0);
+      float pv[16];
+      float ps = 0.f;
+      u32x4 ka[PD + 1];
+#pragma unroll
+      for (int c = 0; c < PD; ++c) ka[c] = kread(1, c);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + PD < NC) ka[(c + PD) % (PD + 1)] = kread(1, c + PD);
+        __builtin_amdgcn_sched_barrier(0);
+        s1 = mfma(ka[c % (PD + 1)], qf[c], c == 0 ? f32x16{} : s1);
+        // softmax(S0): the max after the first MFMA (S0's last result has
+        // landed by then), the exponentials spread over the rest
+        if (c == 0) R0 = softmax_max(s0);
+        if (c >= 1) softmax_exp(s0, R0.msub, pv, ps, 16 * (c - 1) / (NC - 1), 16 * c / (NC - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lsum = lsum * R0.alpha + ps;
+      pack_half(pv, pf[0][0], pf[0][1]);
+      pin(pf[0][0], pf[0][1], lsum);
+    }
+    if (R0.any) rescale_o(R0.alpha);
+    if (!ct.full) mask_half(s1, 1, ct);
+
+    // ---- PV0 | softmax(S1) ----
+    {
+      float pv[16];
+      float ps = 0.f;
+      u32x4 va[PD + 1];
+#pragma unroll
+      for (int st = 0; st < PD; ++st) va[st] = vread(0, st);
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) {
-        if (st + 1 < NSTEP) va[(st + 1) & 1] = vread(1, st + 1);
+        if (st + PD < NSTEP) va[(st + PD) % (PD + 1)] = vread(0, st + PD);
+        __builtin_amdgcn_sched_barrier(0);
         const int hh = st / NDB, db = st % NDB;
-        o[db] = mfma(va[st & 1], pf[1][hh], o[db]);
+        o[db] = mfma(va[st % (PD + 1)], pf[0][hh], o[db]);
+        if (st == 0) R1 = softmax_max(s1);
+        if (st >= 1) softmax_exp(s1, R1.msub, pv, ps, 16 * (st - 1) / (NSTEP - 1), 16 * st / (NSTEP - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lsum = lsum * R1.alpha + ps;
+      pack_half(pv, pf[1][0], pf[1][1]);
+      pin(pf[1][0], pf[1][1], lsum);
+    }
+    if (R1.any) rescale_o(R1.alpha);
+
+    // ---- PV1 ----
+    {
+      u32x4 va[PD + 1];
+#pragma unroll
+      for (int st = 0; st < PD; ++st) va[st] = vread(1, st);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + PD < NSTEP) va[(st + PD) % (PD + 1)] = vread(1, st + PD);
+        __builtin_amdgcn_sched_barrier(0);
+        const int hh = st / NDB, db = st % NDB;
+        o[db] = mfma(va[st % (PD + 1)], pf[1][hh], o[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
