@@ -32,12 +32,20 @@
 // operand reads are free of bank conflicts; the swizzle is applied by choosing
 // which global unit each lane copies.
 //
-// Exponentials run in base 2 with scale*log2(e) folded into one FMA.  The
-// reference max used for the exponentials is only raised when the tile max
-// exceeds it by more than 2^8 (lazy rescale): the identity holds for any
-// reference value, p stays <= 256 (exact range for bf16 and fp32 sums), and
-// the rescale of o is skipped for most tiles.  The exact running max is
-// tracked beside it and applied before the state leaves the kernel.
+// Exponentials run in base 2 with scale*log2(e) folded into one FMA, against
+// a per-row reference m2 instead of the exact running max: the rescaling
+// identity holds for any reference, so the reference only has to keep p
+// finite and exact in range.  Two modes:
+//  * the state leaves the kernel (block step): m2 is raised to the tile max
+//    only when that exceeds it by more than 2^8 (lazy rescale, p <= 256);
+//    the exact running max is tracked beside it and applied at the end;
+//  * only out and lse leave the kernel (whole ring): no row max is taken at
+//    all.  The exponentials use m2 as it stands, and a half-tile whose
+//    per-lane sum of p exceeds 2^64 (or is non-zero while m2 is still -inf)
+//    is redone after raising m2 to the row max, with l and o rescaled.
+//    out and lse do not depend on the reference.
+// Either way the rescale of o sits behind a wave-uniform branch that is
+// rarely taken.
 //
 // Causal masking on global positions (key visible iff pos_k <= pos_q).  With
 // device-ordered data (POS_ANALYTIC) positions are computed from the layout
@@ -45,6 +53,8 @@
 // tile's last position are skipped and tiles wholly before its first
 // position run without a mask.  With explicit position arrays (POS_ARRAY)
 // every tile is classified from the min/max of its key positions.
+#include <utility>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -63,6 +73,7 @@ typedef __attribute__((address_space(3))) char lds_t;
 
 constexpr int BN = 64;            // keys per tile
 constexpr float kLazy = 8.0f;     // log2 of the largest p admitted before rescaling
+constexpr float kBig = 64.0f;     // same, for the checked mode (no row max per tile)
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -104,6 +115,18 @@ __device__ inline int wave_max(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
   return v;
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1,
+// each call inlined (the step sequences below index registers by i).
+template <typename F, int... Is>
+__device__ __attribute__((always_inline)) inline void static_for_impl(
+    F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // A key tile to process: keys [start, start + n) of the Sk_tot axis, from key
@@ -221,7 +244,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index, uniform across the wave (kept in a scalar register)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31;
   const int hi = lane >> 5;
 
@@ -286,6 +310,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   //      mtrue (exact base-2 running max), lsum (this lane's partial sum) ----
   f32x16 o[NDB];
   float m2 = -__builtin_inff(), mtrue = -__builtin_inff(), lsum = 0.f;
+  // Checked mode (the state does not leave the kernel, so only out and lse,
+  // which do not depend on the reference, are produced): the exponentials use
+  // the current reference m2 directly and no row max is taken; a half whose
+  // per-lane sum exceeds plim (p possibly above 2^kBig, or any p > 0 while
+  // m2 is still -inf) is redone after raising m2 to the row max.
+  float msub = 0.f;  // reference subtracted in the exponentials (0 while m2 = -inf)
+  float plim = 0.f;  // largest admitted per-lane sum of a half
   const int64_t srow = bh * P.Sq_tot + qrow;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -324,21 +355,44 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     vofs0 = vkey * ROWB + ((u ^ vswz(vkey)) << 4) + ((lane & 1) << 3);
   }
 
-  // ---- tile copy: HBM -> LDS, swizzled, rows past the tile end clamped;
-  //      uniform tile base + 32-bit lane offset ----
+  // ---- tile copy: HBM -> LDS, swizzled.  Copy x = wave + NW*i moves 64
+  //      units of 16 bytes: rows x*RPC + lane/UNITS, unit lane%UNITS.  Both
+  //      swizzles only depend on row bits that copy i = 0 already fixes
+  //      (NW*RPC rows later the pattern repeats), so a full tile's source
+  //      offsets are this lane's offset for i = 0 plus i*NW*1024: a uniform
+  //      base and a 32-bit lane offset per copy.  Rows past a ragged tile's
+  //      end are clamped to its last row. ----
+  constexpr int RPC = 64 / UNITS;  // rows per 1 KB copy
+  static_assert((NW * RPC) % (KMASK + 1) == 0 && (NW * RPC) % 4 == 0,
+                "swizzle period must divide the rows between a wave's copies");
+  unsigned dk0, dv0;
+  {
+    const int row = wave * RPC + lane / UNITS;
+    const int ph = lane % UNITS;
+    dk0 = row * ROWB + ((ph ^ (row & KMASK)) << 4);
+    dv0 = row * ROWB + ((ph ^ vswz(row)) << 4);
+  }
   auto issue_tile = [&](const Tile& T, lds_t* kdst) {
     lds_t* vdst = kdst + TILE_BYTES;
     const char* kb = reinterpret_cast<const char*>(Kg + T.start * D);
     const char* vb = reinterpret_cast<const char*>(Vg + T.start * D);
+    if (T.n == BN) {
 #pragma unroll
-    for (int i = 0; i < XPW; ++i) {
-      const int x = wave + NW * i;
-      const int U = x * 64 + lane;
-      const int row = U / UNITS;
-      const int ph = U % UNITS;
-      const int rb = min(row, T.n - 1) * ROWB;
-      dma16(kb + rb + ((ph ^ (row & KMASK)) << 4), kdst + x * 1024);
-      dma16(vb + rb + ((ph ^ vswz(row)) << 4), vdst + x * 1024);
+      for (int i = 0; i < XPW; ++i) {
+        const int x = wave + NW * i;
+        dma16(kb + i * NW * 1024 + dk0, kdst + x * 1024);
+        dma16(vb + i * NW * 1024 + dv0, vdst + x * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < XPW; ++i) {
+        const int x = wave + NW * i;
+        const int row = x * RPC + lane / UNITS;
+        const int ph = lane % UNITS;
+        const int rb = min(row, T.n - 1) * ROWB;
+        dma16(kb + rb + ((ph ^ (row & KMASK)) << 4), kdst + x * 1024);
+        dma16(vb + rb + ((ph ^ vswz(row)) << 4), vdst + x * 1024);
+      }
     }
   };
 
@@ -349,7 +403,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   if (have) issue_tile(cur, smem);
   wait_dma();
   __syncthreads();
-  int buf = 0;
 
   // Causal / ragged mask of one 32-key half (partial tiles only).
   auto mask_half = [&](f32x16& sa, int kb, const Tile& T) {
@@ -371,10 +424,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
 
   // ---- online softmax of one 32-key half, split so that its pieces can be
   //      placed between MFMAs (base 2, lazy rescale) ----
-  // Part 1 (row max and the rescale decision): updates m2 and mtrue; returns
-  // the factor for o and l, and the reference subtracted in the exponentials.
+  // Part 1 (row max and the rescale decision): updates m2 and mtrue and
+  // returns the reference subtracted in the exponentials, the previous
+  // reference and whether any lane of the wave raised its reference.
   struct Ref {
-    float alpha, msub;
+    float msub, mold;
     bool any;
   };
   auto softmax_max = [&](const f32x16& sa) {
@@ -389,10 +443,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     const float tm2 = tmax * P.sl2;
     mtrue = fmaxf(mtrue, tm2);
     const bool need = tm2 > m2 + kLazy;
-    const float mnew = need ? tm2 : m2;
     Ref R;
-    R.alpha = need ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.0f;
-    m2 = mnew;
+    R.mold = m2;
+    m2 = need ? tm2 : m2;
     R.any = __any(need);
     R.msub = m2 > -__builtin_inff() ? m2 : 0.f;
     return R;
@@ -410,6 +463,54 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     pf1 = u32x4{pack2(pv[8], pv[9]), pack2(pv[10], pv[11]), pack2(pv[12], pv[13]),
                 pack2(pv[14], pv[15])};
   };
+  // Part 3, once the half's sum is known: rescale l and o when the wave
+  // raised a reference (rare under the lazy rule, so the factor and the
+  // multiplications sit behind a wave-uniform branch), then add the sum.
+  auto softmax_close = [&](const Ref& R, float ps) {
+    if (R.any) {
+      // 1 where this lane kept its reference (also when both are -inf)
+      const float alpha = R.mold == m2 ? 1.0f : __builtin_amdgcn_exp2f(R.mold - m2);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    lsum += ps;
+  };
+
+  // Checked mode, end of a half: if a lane's sum is out of range (or NaN),
+  // the wave takes the pair max, raises m2 where it is exceeded, redoes the
+  // half's exponentials and rescales l and o; then the sum joins l.
+  auto softmax_check = [&](const f32x16& sa, float* pv, float& ps) {
+    if (__any(!(ps <= plim))) {
+      float tmax = sa[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sa[i]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                       false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float tm2 = tmax * P.sl2;
+      const bool raise = tm2 > m2;
+      const float mnew = raise ? tm2 : m2;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.0f;
+      m2 = mnew;
+      msub = m2 > -__builtin_inff() ? m2 : 0.f;
+      plim = m2 > -__builtin_inff() ? __builtin_amdgcn_exp2f(kBig) : 0.f;
+      ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], P.sl2, -msub));
+        ps += pv[e];
+      }
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    lsum += ps;
+  };
 
   // Keeps a softmax result in the region where it is written (an empty asm
   // that reads it), so the compiler cannot sink the exponentials below the
@@ -418,136 +519,131 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     asm volatile("" ::"v"(a), "v"(c), "v"(x));
   };
 
-  auto rescale_o = [&](float alpha) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-  };
-
   // One tile: copy the next tile into `nb` while computing on `cb`.  The two
   // restrict-qualified buffers tell the compiler the copy cannot alias the
   // operand reads, so no wait for the copy is placed before them.
-  // Program order per wave (MFMA and VALU of one wave overlap in hardware;
-  // every LDS operand read is issued two MFMAs before its use; the fences
-  // keep the compiler from reordering across these points):
+  // The tile is one sequence of MFMA steps per wave:
   //   S0 = K[0:32] . Q^T            | next tile's copy issue
-  //   S1 = K[32:64] . Q^T           | softmax(S0) in 6 pieces
-  //   O^T += V[0:32]^T . P0^T       | softmax(S1) in 6 pieces
+  //   S1 = K[32:64] . Q^T           | softmax(S0) in pieces
+  //   O^T += V[0:32]^T . P0^T       | softmax(S1) in pieces
   //   O^T += V[32:64]^T . P1^T
-  constexpr int PD = 2;  // operand read distance, in MFMAs
+  // and the LDS operand of step s + PD is read at step s, across the section
+  // boundaries (MFMA and VALU of one wave overlap in hardware; the fences
+  // keep the compiler from reordering across the steps).
+  constexpr int PD = 3;  // operand read distance, in MFMAs
   auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& ct,
                   const Tile& nt, bool have_next) {
     const lds_t* Kb = cb;
     const lds_t* Vb = cb + TILE_BYTES;
-    auto kread = [&](int kb, int c) {
-      return lds_read128(Kb + (kofs0 ^ (c << 5)) + kb * 32 * ROWB);
-    };
-    constexpr int NSTEP = 2 * NDB;  // (half, d block) PV steps per 32 keys
-    auto vread = [&](int kb, int st) {
-      const int hh = st / NDB, db = st % NDB;
+    constexpr int NSTEP = 2 * NDB;           // (half, d block) PV steps per 32 keys
+    constexpr int NS = 2 * NC + 2 * NSTEP;   // MFMAs per tile and wave
+    auto operand = [&](int st) -> u32x4 {
+      if (st < 2 * NC) {  // K rows 32*kb .. +32, d chunk c
+        const int kb = st / NC, c = st % NC;
+        return lds_read128(Kb + (kofs0 ^ (c << 5)) + kb * 32 * ROWB);
+      }
+      const int v = st - 2 * NC;  // V^T: key half kb, 16-key group hh, d block db
+      const int kb = v / NSTEP, hh = (v % NSTEP) / NDB, db = v % NDB;
       const lds_t* vp = Vb + (vofs0 ^ (db << 6)) + (32 * kb + 16 * hh) * ROWB;
       const u32x2 x0 = lds_read_tr(vp);
       const u32x2 x1 = lds_read_tr(vp + 8 * ROWB);
       return u32x4{x0.x, x0.y, x1.x, x1.y};
     };
 
-    // ---- S0, the next tile's copy issued halfway ----
     f32x16 s0, s1;
-    {
-      u32x4 ka[PD + 1];
-#pragma unroll
-      for (int c = 0; c < PD; ++c) ka[c] = kread(0, c);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + PD < NC) ka[(c + PD) % (PD + 1)] = kread(0, c + PD);
-        __builtin_amdgcn_sched_barrier(0);
-        s0 = mfma(ka[c % (PD + 1)], qf[c], c == 0 ? f32x16{} : s0);
-        if (c == NC / 2) issue_tile(have_next ? nt : ct, nb);  // last tile re-copies itself
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (!ct.full) mask_half(s0, 0, ct);
-
-    // ---- S1 | softmax(S0) ----
     u32x4 pf[2][2];
     Ref R0, R1;
-    {
-      float pv[16];
-      float ps = 0.f;
-      u32x4 ka[PD + 1];
-#pragma unroll
-      for (int c = 0; c < PD; ++c) ka[c] = kread(1, c);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + PD < NC) ka[(c + PD) % (PD + 1)] = kread(1, c + PD);
-        __builtin_amdgcn_sched_barrier(0);
-        s1 = mfma(ka[c % (PD + 1)], qf[c], c == 0 ? f32x16{} : s1);
+    float pv0[16], pv1[16];
+    float ps0 = 0.f, ps1 = 0.f;
+    u32x4 opd[PD + 1];
+    static_for<PD>([&](auto I) __attribute__((always_inline)) {
+      constexpr int st = decltype(I)::value;
+      opd[st] = operand(st);
+    });
+    static_for<NS>([&](auto I) __attribute__((always_inline)) {
+      constexpr int st = decltype(I)::value;
+      if constexpr (st + PD < NS) opd[(st + PD) % (PD + 1)] = operand(st + PD);
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 a = opd[st % (PD + 1)];
+      if constexpr (st < NC) {
+        s0 = mfma(a, qf[st], st == 0 ? f32x16{} : s0);
+        if constexpr (st == NC / 2) issue_tile(have_next ? nt : ct, nb);  // last tile re-copies itself
+      } else if constexpr (st < 2 * NC) {
+        constexpr int c = st - NC;
+        s1 = mfma(a, qf[c], c == 0 ? f32x16{} : s1);
         // softmax(S0): the max after the first MFMA (S0's last result has
         // landed by then), the exponentials spread over the rest
-        if (c == 0) R0 = softmax_max(s0);
-        if (c >= 1) softmax_exp(s0, R0.msub, pv, ps, 16 * (c - 1) / (NC - 1), 16 * c / (NC - 1));
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (c == 0) {
+          if constexpr (STATE_IO) R0 = softmax_max(s0);
+        }
+        if constexpr (c >= 1)
+          softmax_exp(s0, STATE_IO ? R0.msub : msub, pv0, ps0, 16 * (c - 1) / (NC - 1),
+                      16 * c / (NC - 1));
+      } else if constexpr (st < 2 * NC + NSTEP) {
+        constexpr int v = st - 2 * NC, hh = v / NDB, db = v % NDB;
+        o[db] = mfma(a, pf[0][hh], o[db]);
+        if constexpr (v == 0) {
+          if constexpr (STATE_IO) R1 = softmax_max(s1);
+        }
+        if constexpr (v >= 1)
+          softmax_exp(s1, STATE_IO ? R1.msub : msub, pv1, ps1, 16 * (v - 1) / (NSTEP - 1),
+                      16 * v / (NSTEP - 1));
+      } else {
+        constexpr int v = st - 2 * NC - NSTEP, hh = v / NDB, db = v % NDB;
+        o[db] = mfma(a, pf[1][hh], o[db]);
       }
-      lsum = lsum * R0.alpha + ps;
-      pack_half(pv, pf[0][0], pf[0][1]);
-      pin(pf[0][0], pf[0][1], lsum);
-    }
-    if (R0.any) rescale_o(R0.alpha);
-    if (!ct.full) mask_half(s1, 1, ct);
-
-    // ---- PV0 | softmax(S1) ----
-    {
-      float pv[16];
-      float ps = 0.f;
-      u32x4 va[PD + 1];
-#pragma unroll
-      for (int st = 0; st < PD; ++st) va[st] = vread(0, st);
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        if (st + PD < NSTEP) va[(st + PD) % (PD + 1)] = vread(0, st + PD);
-        __builtin_amdgcn_sched_barrier(0);
-        const int hh = st / NDB, db = st % NDB;
-        o[db] = mfma(va[st % (PD + 1)], pf[0][hh], o[db]);
-        if (st == 0) R1 = softmax_max(s1);
-        if (st >= 1) softmax_exp(s1, R1.msub, pv, ps, 16 * (st - 1) / (NSTEP - 1), 16 * st / (NSTEP - 1));
-        __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (st == NC - 1) {
+        if (!ct.full) mask_half(s0, 0, ct);
+      } else if constexpr (st == 2 * NC - 1) {
+        if constexpr (STATE_IO) {
+          pack_half(pv0, pf[0][0], pf[0][1]);
+          pin(pf[0][0], pf[0][1], ps0);
+          softmax_close(R0, ps0);
+        } else {
+          softmax_check(s0, pv0, ps0);
+          pack_half(pv0, pf[0][0], pf[0][1]);
+        }
+        if (!ct.full) mask_half(s1, 1, ct);
+      } else if constexpr (st == 2 * NC + NSTEP - 1) {
+        if constexpr (STATE_IO) {
+          pack_half(pv1, pf[1][0], pf[1][1]);
+          pin(pf[1][0], pf[1][1], ps1);
+          softmax_close(R1, ps1);
+        } else {
+          softmax_check(s1, pv1, ps1);
+          pack_half(pv1, pf[1][0], pf[1][1]);
+        }
       }
-      lsum = lsum * R1.alpha + ps;
-      pack_half(pv, pf[1][0], pf[1][1]);
-      pin(pf[1][0], pf[1][1], lsum);
-    }
-    if (R1.any) rescale_o(R1.alpha);
-
-    // ---- PV1 ----
-    {
-      u32x4 va[PD + 1];
-#pragma unroll
-      for (int st = 0; st < PD; ++st) va[st] = vread(1, st);
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        if (st + PD < NSTEP) va[(st + PD) % (PD + 1)] = vread(1, st + PD);
-        __builtin_amdgcn_sched_barrier(0);
-        const int hh = st / NDB, db = st % NDB;
-        o[db] = mfma(va[st % (PD + 1)], pf[1][hh], o[db]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
+  // The loop body is written out once per LDS buffer, so that every operand
+  // read and copy destination has a constant buffer offset.
   while (have) {
-    Tile nxt;
-    const bool have_next = walker.next(P, dev, qmin, qmax, nxt);
-    tile(smem + buf * (2 * TILE_BYTES), smem + (buf ^ 1) * (2 * TILE_BYTES), cur, nxt, have_next);
-    wait_dma();
-    __syncthreads();
-    buf ^= 1;
-    cur = nxt;
-    have = have_next;
+    {
+      Tile nxt;
+      const bool have_next = walker.next(P, dev, qmin, qmax, nxt);
+      tile(smem, smem + 2 * TILE_BYTES, cur, nxt, have_next);
+      wait_dma();
+      __syncthreads();
+      cur = nxt;
+      if (!have_next) break;
+    }
+    {
+      Tile nxt;
+      const bool have_next = walker.next(P, dev, qmin, qmax, nxt);
+      tile(smem + 2 * TILE_BYTES, smem, cur, nxt, have_next);
+      wait_dma();
+      __syncthreads();
+      cur = nxt;
+      have = have_next;
+    }
   }
 
   // ---- epilogue ----
-  if (mtrue > -__builtin_inff() && mtrue != m2) {  // move to the exact running max
+  if (STATE_IO && mtrue > -__builtin_inff() && mtrue != m2) {  // move to the exact running max
     const float alpha = __builtin_amdgcn_exp2f(m2 - mtrue);
     lsum *= alpha;
 #pragma unroll

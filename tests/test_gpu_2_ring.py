@@ -166,3 +166,26 @@ def test_deterministic():
     a = run_ring(q, k, v, N, "zigzag", True)
     b = run_ring(q, k, v, N, "zigzag", True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_jumps(layout, causal):
+    """Keys in every third 64-key tile are scaled by 30, so a row's scores
+    jump by far more than 2^64 in base-2 units between tiles in every ring
+    order: the kernels must rescale the running state mid-stream (and never
+    let an exponential overflow).  The peaked rows make each output close to
+    a single value row, so V is drawn with standard deviation 1/4: bf16
+    rounding of an output near 4 alone costs up to 0.016 of the absolute
+    tolerance, while a wrong rescale shows up at the size of V itself."""
+    B, Hq, Hkv, S, N, D = 1, 4, 2, 1536, 4, 128
+    q = rand((B, Hq, S, D), 61, torch.float32)
+    k = rand((B, Hkv, S, D), 62, torch.float32)
+    v = rand((B, Hkv, S, D), 63, torch.float32) * 0.25
+    f = np.where((np.arange(S) // 64) % 3 == 2, 30.0, 1.0)
+    k = k * torch.from_numpy(f).float()[None, None, :, None]
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    out, lse = run_ring(q, k, v, N, layout, causal)
+    ro, rl = O1.full_attention(q, k, v, causal=causal)
+    assert float(np.max(rl)) > 40.0  # some rows meet scores far above their earlier tiles
+    check(out, lse, ro, rl, torch.bfloat16, f"score jumps {layout} causal={causal}")
