@@ -8,7 +8,9 @@
 //
 // Work split.  A workgroup owns BM = 32*NW query rows of one (batch, query
 // head) and walks the key/value blocks in ring order, 64 keys per tile; each
-// of its NW waves owns 32 query rows.  Per tile and wave:
+// of its NW waves owns 32 query rows (NW = 8 for head dim 128: one 512-thread
+// workgroup per CU, two waves per SIMD, each key/value tile shared by 256
+// query rows; NW = 4 below, two workgroups per CU).  Per tile and wave:
 //   S^T[64 keys x 32 queries] = K_tile . Q^T   v_mfma_f32_32x32x16_bf16,
 //        A = K rows read from LDS, B = Q^T fragments held in registers;
 //   softmax on S^T: every lane holds 32 scores of ONE query (the other 32 of
@@ -380,8 +382,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
 #pragma unroll
       for (int i = 0; i < XPW; ++i) {
         const int x = wave + NW * i;
-        dma16(kb + i * NW * 1024 + dk0, kdst + x * 1024);
-        dma16(vb + i * NW * 1024 + dv0, vdst + x * 1024);
+        // The copy's constant goes into the 32-bit lane offset, which the
+        // empty asm makes opaque: the address stays "scalar base + 32-bit
+        // offset" (global_load_lds with saddr).  Left to itself the compiler
+        // shares one 64-bit per-lane address between the copies and adds the
+        // constants in 64-bit VALU arithmetic, and the 64-bit-address form of
+        // the copy stalls the MFMAs around it.
+        unsigned ko = dk0 + i * NW * 1024, vo = dv0 + i * NW * 1024;
+        asm volatile("" : "+v"(ko), "+v"(vo));
+        dma16(kb + ko, kdst + x * 1024);
+        dma16(vb + vo, vdst + x * 1024);
       }
     } else {
 #pragma unroll
@@ -390,8 +400,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
         const int row = x * RPC + lane / UNITS;
         const int ph = lane % UNITS;
         const int rb = min(row, T.n - 1) * ROWB;
-        dma16(kb + rb + ((ph ^ (row & KMASK)) << 4), kdst + x * 1024);
-        dma16(vb + rb + ((ph ^ vswz(row)) << 4), vdst + x * 1024);
+        unsigned ko = rb + ((ph ^ (row & KMASK)) << 4), vo = rb + ((ph ^ vswz(row)) << 4);
+        asm volatile("" : "+v"(ko), "+v"(vo));
+        dma16(kb + ko, kdst + x * 1024);
+        dma16(vb + vo, vdst + x * 1024);
       }
     }
   };
@@ -723,7 +735,7 @@ hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mod
   switch (D) {
     case 32: return launch_d<32, 4>(p, causal, pos_mode, state_io, s);
     case 64: return launch_d<64, 4>(p, causal, pos_mode, state_io, s);
-    case 128: return launch_d<128, 4>(p, causal, pos_mode, state_io, s);
+    case 128: return launch_d<128, 8>(p, causal, pos_mode, state_io, s);  // 1 KB copies need D*16 >= NW KB
     default: return hipErrorInvalidValue;
   }
 }
