@@ -70,11 +70,19 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa32k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target oracle time for the CPU baseline sample")
+    ap.add_argument("--step-sweep", action="store_true",
+                    help="state-in-HBM ra_block_step on the 32K-token, 32/8-head query set cut "
+                         "into blocks of 128..1024 tokens (HBM GB/s); one JSON line per block size")
+    ap.add_argument("--layout-balance", action="store_true",
+                    help="the 64K causal case per layout: whole ring, permute / un-permute GB/s, "
+                         "each virtual device's share and the simulated ring makespan")
+    ap.add_argument("--tiny", action="store_true",
+                    help="the pages' 4 x 3 tokens x d=8 case: microseconds per ra_ring call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (contiguous ra_permute) so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -171,6 +179,153 @@ def cpu_baseline(q, k, v, cfg, layout, device, seconds, gpu_out=None, gpu_lse=No
     }, errs
 
 
+def timed(fn, steps, warmup, stream):
+    """Mean ms of fn() over `steps` launches, HIP events on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def step_sweep(args):
+    """ra_block_step with the state in HBM (fp32 m, l, acc read and written
+    per step), non-causal, on the 32768-token x 32/8-head x D=128 query set cut
+    into `batch` = 32768/blk independent blocks of blk tokens, each folding one
+    key/value block of blk tokens.  Bytes per step are algorithmic: Q read,
+    K and V read, acc/m/l read and written."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+
+    Hq, Hkv, D, total = 32, 8, 128, 32768
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda")
+    for blk in (128, 256, 512, 1024):
+        g.manual_seed(blk)
+        batch = total // blk
+        q = torch.randn((batch, Hq, blk, D), generator=g, device="cuda").to(torch.bfloat16)
+        k = torch.randn((batch, Hkv, blk, D), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((batch, Hkv, blk, D), generator=g, device="cuda").to(torch.bfloat16)
+        st = ra.State(batch, Hq, blk, D)
+        ra.ra_state_init(st)
+
+        def step():
+            ra.ra_block_step(q, k, v, None, None, ra.RA_MASK_NONE, st, stream=stream)
+
+        ms = timed(step, args.steps, args.warmup, stream)
+        nbytes = batch * blk * (Hq * (2 * D + 8 * D + 16) + Hkv * 2 * 2 * D)
+        flops = 4.0 * D * Hq * batch * blk * blk
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": "ra_block_step HBM GB/s (state in HBM, small blocks)", "block_tokens": blk,
+            "batch": batch, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "dtype": "bf16",
+            "us_per_step": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "tflop_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
+            "flop_per_byte": round(flops / nbytes, 1), "steps": args.steps, "data": "synthetic"}),
+            flush=True)
+        del q, k, v, st
+        torch.cuda.empty_cache()
+
+
+def layout_balance(args):
+    """The 64K-token causal ring (32/8 heads, D=128, N=8) under each layout:
+    the whole ring on one GPU (device = -1, permute + fused ring + un-permute),
+    the permute and un-permute passes alone, and each virtual device's share
+    (device = p) whose maximum is the makespan of an N-GPU ring that overlaps
+    its key/value passes."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+    import workloads
+
+    cfg = workloads.WORKLOADS["gqa64k"]
+    S, N, D, Hq, Hkv = cfg["S"], cfg["N"], cfg["D"], cfg["Hq"], cfg["Hkv"]
+    blk = S // N
+    print("# generating inputs for gqa64k", file=sys.stderr, flush=True)
+    q, k, v = workloads.workload_inputs("gqa64k")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    del q, k, v
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    for layout in ("contiguous", "striped", "zigzag"):
+        nws = ra.ra_ring_workspace_bytes(qd, kd, N, layout, -1)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        t_whole = timed(lambda: ra.ra_ring(qd, kd, vd, out, lse, N, layout, True, -1, ws,
+                                           stream=stream), args.steps, args.warmup, stream)
+        rec = {"metric": "causal ring layout balance (64K tokens, N=8)", "layout": layout,
+               "whole_ring_ms": round(t_whole, 3)}
+        # device-order copies of Q, K, V (the shares' inputs); permute / un-permute timing
+        qp, kp, vp = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        if layout != "contiguous":
+            def fwd():
+                ra.ra_permute(qd.view(Hq, S, D), qp.view(Hq, S, D), N, layout, stream=stream)
+                ra.ra_permute(kd.view(Hkv, S, D), kp.view(Hkv, S, D), N, layout, stream=stream)
+                ra.ra_permute(vd.view(Hkv, S, D), vp.view(Hkv, S, D), N, layout, stream=stream)
+
+            t_f = timed(fwd, args.steps, args.warmup, stream)
+            fbytes = 2 * 2 * S * D * (Hq + 2 * Hkv)
+            inv_out = torch.empty_like(qd)
+            lse2 = torch.empty_like(lse)
+
+            def inv():
+                ra.ra_permute(qp.view(Hq, S, D), inv_out.view(Hq, S, D), N, layout, inverse=True,
+                              stream=stream)
+                ra.ra_permute(lse.view(Hq, S, 1), lse2.view(Hq, S, 1), N, layout, inverse=True,
+                              stream=stream)
+            t_i = timed(inv, args.steps, args.warmup, stream)
+            ibytes = 2 * (2 * S * D * Hq + 4 * S * Hq)
+            rec.update({"permute_ms": round(t_f, 3), "permute_gb_per_s": round(fbytes / (t_f * 1e-3) / 1e9, 1),
+                        "unpermute_ms": round(t_i, 3),
+                        "unpermute_gb_per_s": round(ibytes / (t_i * 1e-3) / 1e9, 1)})
+        else:
+            qp.copy_(qd), kp.copy_(kd), vp.copy_(vd)
+        dev_ms = []
+        oshare = torch.empty((1, Hq, blk, D), dtype=qd.dtype, device="cuda")
+        lshare = torch.empty((1, Hq, blk), dtype=torch.float32, device="cuda")
+        for p in range(N):
+            qs = qp[:, :, p * blk:(p + 1) * blk].contiguous()
+            t = timed(lambda: ra.ra_ring(qs, kp, vp, oshare, lshare, N, layout, True, p, None,
+                                         stream=stream), max(2, args.steps // 2), 2, stream)
+            dev_ms.append(round(t, 3))
+        mk = max(dev_ms)
+        rec.update({"device_share_ms": dev_ms, "makespan_ms": mk,
+                    "imbalance_max_over_mean": round(mk / float(np.mean(dev_ms)), 3),
+                    "tokens_per_s_one_gpu": round(S / (t_whole * 1e-3), 1),
+                    "tokens_per_s_projected_ring": round(S / (mk * 1e-3), 1)})
+        print(json.dumps(rec), flush=True)
+        del qp, kp, vp, ws
+        torch.cuda.empty_cache()
+
+
+def tiny_latency(args):
+    """The pages' tiny case (4 devices x 3 tokens, d = 8, fp32, non-causal):
+    microseconds per ra_ring call, HIP events on the launch stream."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+    import workloads
+
+    q, k, v = (t.cuda() for t in workloads.workload_inputs("tiny"))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = timed(lambda: ra.ra_ring(q, k, v, out, lse, 4, "contiguous", False, -1, None,
+                                  stream=stream), 1000, 50, stream)
+    print(json.dumps({"metric": "ra_ring latency, pages' tiny case (N=4 x 3 tokens, d=8, fp32)",
+                      "us_per_call": round(ms * 1e3, 2), "calls": 1000}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -188,6 +343,15 @@ def main():
         sys.exit(3)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.step_sweep:
+        step_sweep(args)
+        return
+    if args.layout_balance:
+        layout_balance(args)
+        return
+    if args.tiny:
+        tiny_latency(args)
         return
     wkey, layout, device = WORKLOADS[args.workload]
     cfg = workloads.WORKLOADS[wkey]

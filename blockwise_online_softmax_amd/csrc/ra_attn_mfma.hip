@@ -8,9 +8,10 @@
 //
 // Work split.  A workgroup owns BM = 32*NW query rows of one (batch, query
 // head) and walks the key/value blocks in ring order, 64 keys per tile; each
-// of its NW waves owns 32 query rows (NW = 8 for head dim 128: one 512-thread
-// workgroup per CU, two waves per SIMD, each key/value tile shared by 256
-// query rows; NW = 4 below, two workgroups per CU).  Per tile and wave:
+// of its NW waves owns 32 query rows (NW = 8 for head dim 128 and query
+// blocks of at least 256 rows: one 512-thread workgroup per CU, two waves per
+// SIMD, each key/value tile shared by 256 query rows; otherwise NW = 4, two
+// workgroups per CU).  Per tile and wave:
 //   S^T[64 keys x 32 queries] = K_tile . Q^T   v_mfma_f32_32x32x16_bf16,
 //        A = K rows read from LDS, B = Q^T fragments held in registers;
 //   softmax on S^T: every lane holds 32 scores of ONE query (the other 32 of
@@ -735,7 +736,9 @@ hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mod
   switch (D) {
     case 32: return launch_d<32, 4>(p, causal, pos_mode, state_io, s);
     case 64: return launch_d<64, 4>(p, causal, pos_mode, state_io, s);
-    case 128: return launch_d<128, 8>(p, causal, pos_mode, state_io, s);  // 1 KB copies need D*16 >= NW KB
+    case 128:  // 8 waves (256 query rows) once a block has that many rows
+      return p.qlen >= 256 ? launch_d<128, 8>(p, causal, pos_mode, state_io, s)
+                           : launch_d<128, 4>(p, causal, pos_mode, state_io, s);
     default: return hipErrorInvalidValue;
   }
 }
