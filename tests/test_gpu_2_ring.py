@@ -67,13 +67,15 @@ def test_fp32_head_dims(D):
 # bf16: matrix-core kernel for D in {32, 64, 128}, vector kernel for 8, 16.
 BF16_CASES = [
     # (B, Hq, Hkv, S, N, D)
-    (1, 4, 2, 1024, 4, 128),   # several 128-row query tiles and 64-key tiles per block
+    (1, 4, 2, 1024, 4, 128),   # one 256-row query tile and four 64-key tiles per block
     (1, 4, 1, 600, 3, 128),    # ragged: blocks of 200 (not a multiple of 64)
     (2, 2, 2, 512, 8, 64),     # batch 2, MHA, blocks of 64
     (1, 8, 2, 384, 2, 32),     # D = 32
     (1, 2, 1, 136, 4, 16),     # vector kernel (bf16, D = 16), ragged blocks of 34
     (1, 2, 2, 96, 3, 8),       # vector kernel (bf16, D = 8)
     (1, 4, 4, 4096, 8, 128),   # blocks of 512, many tiles
+    (1, 4, 2, 1200, 4, 128),   # blocks of 300: 256-row query tiles with a ragged second tile
+    (1, 2, 1, 1020, 4, 128),   # blocks of 255: the largest block on 128-row query tiles
 ]
 
 
