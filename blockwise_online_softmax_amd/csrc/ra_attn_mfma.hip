@@ -419,6 +419,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
 
   // Causal / ragged mask of one 32-key half (partial tiles only).
   auto mask_half = [&](f32x16& sa, int kb, const Tile& T) {
+    if (CAUSAL && POS == POS_ANALYTIC && T.n == BN && T.split >= BN) {
+      // Full tile with one linear position map (the common case): key kt is
+      // visible iff p0 + kt * stride <= qpos.  With kt = c + 4 hi, c the same
+      // in every lane, that is c * stride <= lim: one compare per element.
+      const int lim = rvalid ? qpos - T.p0 - 4 * hi * T.stride : INT32_MIN;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = kb * 32 + 8 * (i / 4) + (i % 4);
+        sa[i] = c * T.stride <= lim ? sa[i] : -__builtin_inff();
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kt = kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
@@ -429,7 +441,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
           kp = (kt < T.split ? T.p0 : T.p1) + kt * T.stride;
         else
           kp = __shfl(T.kp, kt);
-        vis = vis && (kp <= qpos);
+        vis = vis & (kp <= qpos);
       }
       sa[i] = vis ? sa[i] : -__builtin_inff();
     }
