@@ -83,6 +83,9 @@ def parse():
                          "each virtual device's share and the simulated ring makespan")
     ap.add_argument("--tiny", action="store_true",
                     help="the pages' 4 x 3 tokens x d=8 case: microseconds per ra_ring call")
+    ap.add_argument("--merge", action="store_true",
+                    help="ra_merge and ra_state_merge on the rows of the 32K-token x 32-head "
+                         "x D=128 query set (HBM GB/s); one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (contiguous ra_permute) so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -308,6 +311,51 @@ def layout_balance(args):
         torch.cuda.empty_cache()
 
 
+def merge_bench(args):
+    """ra_merge (bf16 out + fp32 lse) and ra_state_merge (fp32 m, l, acc) on
+    the rows of a 32768-token x 32-head x D=128 query set, two partial
+    results merged into a third buffer.  Bytes are algorithmic: both inputs
+    read once, the output written once."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+
+    B, Hq, S, D = 1, 32, 32768, 128
+    rows = B * Hq * S
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    oa = torch.randn((B, Hq, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    ob = torch.randn((B, Hq, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    la = torch.randn((B, Hq, S), generator=g, device="cuda") * 4
+    lb = torch.randn((B, Hq, S), generator=g, device="cuda") * 4
+    oo, lo = torch.empty_like(oa), torch.empty_like(la)
+    ms = timed(lambda: ra.ra_merge(oa, la, ob, lb, oo, lo, stream=stream), args.steps,
+               args.warmup, stream)
+    nbytes = rows * 3 * (D * 2 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "ra_merge HBM GB/s (bf16 out, fp32 lse)", "rows": rows, "head_dim": D,
+        "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+        "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "steps": args.steps, "data": "synthetic"}), flush=True)
+    del oa, ob, oo, la, lb, lo
+    st = [ra.State(B, Hq, S, D) for _ in range(3)]
+    for i, x in enumerate(st[:2]):
+        x.m.normal_(generator=g).mul_(4)
+        x.l.uniform_(1, 100, generator=g)
+        x.acc.normal_(generator=g)
+    ms = timed(lambda: ra.ra_state_merge(st[0], st[1], st[2], stream=stream), args.steps,
+               args.warmup, stream)
+    nbytes = rows * 3 * (D * 4 + 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "ra_state_merge HBM GB/s (fp32 m, l, acc)", "rows": rows, "head_dim": D,
+        "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+        "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "steps": args.steps, "data": "synthetic"}), flush=True)
+
+
 def tiny_latency(args):
     """The pages' tiny case (4 devices x 3 tokens, d = 8, fp32, non-causal):
     microseconds per ra_ring call, HIP events on the launch stream."""
@@ -352,6 +400,9 @@ def main():
         return
     if args.tiny:
         tiny_latency(args)
+        return
+    if args.merge:
+        merge_bench(args)
         return
     wkey, layout, device = WORKLOADS[args.workload]
     cfg = workloads.WORKLOADS[wkey]

@@ -35,8 +35,8 @@ RA_ZIGZAG = 2
 LAYOUT_IDS = {"contiguous": RA_CONTIGUOUS, "striped": RA_STRIPED, "zigzag": RA_ZIGZAG}
 
 EXPORTED = ["ra_state_init", "ra_block_step", "ra_finalize", "ra_ring",
-            "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_last_error",
-            "ra_version"]
+            "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_state_merge",
+            "ra_merge", "ra_last_error", "ra_version"]
 
 
 class RaDims(ctypes.Structure):
@@ -76,6 +76,8 @@ def load(path=None):
         "ra_ring_workspace_bytes": (sz, [dims_p, i32, i32, i32]),
         "ra_permute": (i32, [vp, vp, i64, i64, i64, i32, i32, i32, vp]),
         "ra_positions": (i32, [vp, i64, i32, i32, i32, vp]),
+        "ra_state_merge": (i32, [state_p, state_p, state_p, vp]),
+        "ra_merge": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "ra_last_error": (ctypes.c_char_p, []),
         "ra_version": (i32, []),
     }
@@ -235,6 +237,31 @@ def ra_positions(pos, S, N, layout, device=-1, stream=None):
     _require(pos, "pos", _torch().int32)
     _check(load().ra_positions(_ptr(pos), int(S), int(N), LAYOUT_IDS.get(layout, layout),
                                int(device), _stream(stream)), "ra_positions")
+
+
+def ra_state_merge(a, b, out, stream=None):
+    """out <- merge of states a and b (out may be a or b)."""
+    sa, sb, so = a.c_struct(), b.c_struct(), out.c_struct()
+    _check(load().ra_state_merge(ctypes.byref(sa), ctypes.byref(sb), ctypes.byref(so),
+                                 _stream(stream)), "ra_state_merge")
+
+
+def ra_merge(out_a, lse_a, out_b, lse_b, out, lse, stream=None):
+    """(out, lse) <- merge of two finalized partial results over disjoint key
+    sets.  out_*: [..., D] of one dtype; lse_*: [...] fp32.  out / lse may be
+    the a or b tensors."""
+    for t, n in ((out_a, "out_a"), (out_b, "out_b"), (out, "out")):
+        _require(t, n, out_a.dtype)
+        if t.shape != out_a.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} differs from {tuple(out_a.shape)}")
+    D = out_a.shape[-1]
+    rows = out_a.numel() // D if D else 0
+    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse, "lse")):
+        _require(t, n, _torch().float32)
+        if t.numel() != rows:
+            raise ValueError(f"{n} has {t.numel()} elements, expected {rows}")
+    _check(load().ra_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out),
+                           _ptr(lse), rows, D, _dtype_id(out_a), _stream(stream)), "ra_merge")
 
 
 def ra_version():

@@ -145,7 +145,7 @@ hipError_t launch_attention(const ra::AttnParams& p, int D, int dtype, bool caus
 
 extern "C" {
 
-int ra_version(void) { return 100; }
+int ra_version(void) { return 101; }
 
 const char* ra_last_error(void) { return g_err; }
 
@@ -215,6 +215,77 @@ ra_status ra_finalize(const ra_state* st, void* out, float* lse, ra_dtype out_dt
   s = hip_status(ra::launch_finalize(st->m, st->l, st->acc, out, lse, st->B * st->Hq * st->Sq,
                                      st->D, out_dtype, (hipStream_t)stream),
                  "ra_finalize launch");
+  return s == RA_OK ? ok() : s;
+}
+
+// A buffer written by a merge either is the input buffer of the same role
+// (in place) or shares no byte with any input buffer or with the other outputs.
+struct span {
+  const void* p;
+  int64_t bytes;
+  int role;
+};
+bool disjoint(const span& x, const span& y) {
+  const uintptr_t a = (uintptr_t)x.p, b = (uintptr_t)y.p;
+  return a + (uintptr_t)x.bytes <= b || b + (uintptr_t)y.bytes <= a;
+}
+bool aliasing_ok(const span* outs, int nout, const span* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (!disjoint(outs[i], ins[j]) && !(outs[i].p == ins[j].p && outs[i].role == ins[j].role))
+        return false;
+    for (int j = 0; j < i; ++j)
+      if (!disjoint(outs[i], outs[j])) return false;
+  }
+  return true;
+}
+
+ra_status ra_state_merge(const ra_state* a, const ra_state* b, const ra_state* out,
+                         void* stream) {
+  ra_status s = check_state(a);
+  if (s == RA_OK) s = check_state(b);
+  if (s == RA_OK) s = check_state(out);
+  if (s != RA_OK) return s;
+  for (const ra_state* x : {b, out})
+    if (x->B != a->B || x->Hq != a->Hq || x->Sq != a->Sq || x->D != a->D)
+      return fail(RA_ERR_SHAPE, "states to merge must have equal B, Hq, Sq, D");
+  const int64_t rows = a->B * a->Hq * a->Sq, vb = rows * 4, ab = rows * a->D * 4;
+  const span ins[6] = {{a->m, vb, 0}, {a->l, vb, 1}, {a->acc, ab, 2},
+                       {b->m, vb, 0}, {b->l, vb, 1}, {b->acc, ab, 2}};
+  const span outs[3] = {{out->m, vb, 0}, {out->l, vb, 1}, {out->acc, ab, 2}};
+  if (!aliasing_ok(outs, 3, ins, 6))
+    return fail(RA_ERR_SHAPE, "ra_state_merge: out overlaps an input other than in place");
+  (void)hipGetLastError();
+  s = hip_status(ra::launch_state_merge(a->m, a->l, a->acc, b->m, b->l, b->acc, out->m, out->l,
+                                        out->acc, rows, a->D,
+                                        (hipStream_t)stream),
+                 "ra_state_merge launch");
+  return s == RA_OK ? ok() : s;
+}
+
+ra_status ra_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
+                   void* out, float* lse, int64_t rows, int64_t D, ra_dtype dtype, void* stream) {
+  if (out_a == nullptr || lse_a == nullptr || out_b == nullptr || lse_b == nullptr ||
+      out == nullptr || lse == nullptr)
+    return fail(RA_ERR_NULL, "ra_merge: every pointer must be non-NULL");
+  if (dtype != RA_F32 && dtype != RA_BF16)
+    return fail(RA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (rows < 1 || rows >= ((int64_t)1 << 40))
+    return fail(RA_ERR_SHAPE, "rows out of range (%lld)", (long long)rows);
+  if (!head_dim_ok(D)) return fail(RA_ERR_UNSUPPORTED, "head dim %lld not supported", (long long)D);
+  const uintptr_t oal = dtype == RA_BF16 ? 8 : 16;
+  if (!aligned(out_a, oal) || !aligned(out_b, oal) || !aligned(out, oal) || !aligned(lse_a, 4) ||
+      !aligned(lse_b, 4) || !aligned(lse, 4))
+    return fail(RA_ERR_SHAPE, "ra_merge: buffers misaligned");
+  const int64_t ob = rows * D * (dtype == RA_BF16 ? 2 : 4), lb = rows * 4;
+  const span ins[4] = {{out_a, ob, 0}, {lse_a, lb, 1}, {out_b, ob, 0}, {lse_b, lb, 1}};
+  const span outs[2] = {{out, ob, 0}, {lse, lb, 1}};
+  if (!aliasing_ok(outs, 2, ins, 4))
+    return fail(RA_ERR_SHAPE, "ra_merge: out / lse overlap an input other than in place");
+  (void)hipGetLastError();
+  ra_status s = hip_status(ra::launch_out_merge(out_a, lse_a, out_b, lse_b, out, lse, rows, D,
+                                                dtype, (hipStream_t)stream),
+                           "ra_merge launch");
   return s == RA_OK ? ok() : s;
 }
 

@@ -69,5 +69,11 @@ hipError_t launch_permute(const void* src, void* dst, int64_t outer, int64_t S, 
                           int N, int layout, int inverse, hipStream_t s);
 hipError_t launch_positions(int32_t* pos, int64_t S, int N, int layout, int device,
                             hipStream_t s);
+hipError_t launch_state_merge(const float* ma, const float* la, const float* acca,
+                              const float* mb, const float* lb, const float* accb, float* mo,
+                              float* lo, float* acco, int64_t rows, int64_t D, hipStream_t s);
+hipError_t launch_out_merge(const void* oa, const float* lsea, const void* ob, const float* lseb,
+                            void* oo, float* lseo, int64_t rows, int64_t D, int dtype,
+                            hipStream_t s);
 
 }  // namespace ra

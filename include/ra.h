@@ -153,6 +153,30 @@ ra_status ra_permute(const void* src, void* dst, int64_t outer, int64_t S, int64
 ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int device,
                        void* stream);
 
+/* Merge two states of the same rows built from disjoint key sets into `out`
+ * ("Module 23", "The Math: One Block at a Time": the fold does not depend on
+ * the order of blocks, so two partial folds combine like one more fold
+ * step): per row, with
+ * m = max(ma, mb), l = la e^(ma-m) + lb e^(mb-m) and
+ * acc = acca e^(ma-m) + accb e^(mb-m).  A side with m = -inf (no visible key)
+ * contributes nothing; a row empty on both sides stays empty.
+ *   a, b, out: states with equal B, Hq, Sq, D.  out may be exactly a or b
+ *   (same buffers); other overlaps are not allowed. */
+ra_status ra_state_merge(const ra_state* a, const ra_state* b, const ra_state* out,
+                         void* stream);
+
+/* Merge two finalized partial results of the same rows over disjoint key sets
+ * ("3.6 Distributed Training II", "Vocab-parallel cross-entropy": logsumexp =
+ * m + log Z, merged across shards): lse = log(e^lse_a + e^lse_b) and
+ * out = out_a e^(lse_a - lse) + out_b e^(lse_b - lse), in out's dtype (round
+ * to nearest even for bf16).  A side with lse = -inf contributes nothing; a
+ * row empty on both sides gets out = 0, lse = -inf.
+ *   out_a, out_b, out: [rows, D] of `dtype`; lse_a, lse_b, lse: [rows] fp32.
+ *   out / lse may be exactly out_a / lse_a or out_b / lse_b; other overlaps
+ *   are not allowed. */
+ra_status ra_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
+                   void* out, float* lse, int64_t rows, int64_t D, ra_dtype dtype, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);
 

@@ -24,6 +24,8 @@ Modules:
   ring       O2: the pages' blockwise recurrence run as a simulated ring.
   layouts    token->device maps (contiguous, striped, zigzag), positions and
              the causal pair count per device.
+  merge      O3: merge of two partial results over disjoint key sets, as
+             running states (m, l, o) or as finalized (out, lse).
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, printed page values, library routines, brute force).  What no
@@ -39,6 +41,7 @@ from .ring import (  # noqa: F401
     ring_visit_order,
     ring_attention,
 )
+from .merge import merge_states, merge_outputs  # noqa: F401
 from .layouts import (  # noqa: F401
     LAYOUTS,
     device_positions,

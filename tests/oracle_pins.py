@@ -11,6 +11,8 @@ Sources (page titles and sections):
          multiple devices?": "The ring", "The causal-mask problem".
   [DT2]  "3.6 Distributed Training II ...": "Ring Attention",
          "Vocab-parallel cross-entropy".
+  O3 (merge) follows [M23] "The Math" (the fold ignores block order) and
+  [DT2] "Vocab-parallel cross-entropy" (max, then sum of rescaled Z).
 """
 
 import json
@@ -384,6 +386,94 @@ def pin_initial_max_reading(o):
     assert _maxdiff(a[0], b[0]) < 1e-12 and _maxdiff(a[1], b[1]) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# O3 merge: two states over disjoint key sets, merged, equal ordinary
+# attention over the union (O1, itself pinned to library routines and brute
+# force above).  The key split is random, not contiguous, and positions are
+# arbitrary, so with the causal rule some rows see keys on one side only and
+# one row (position -1) sees none.
+def pin_merge_equals_full(o):
+    from scipy.special import logsumexp
+
+    rng = np.random.default_rng(111)
+    Sq, Sk, D = 9, 14, 6
+    q = rng.normal(size=(Sq, D)) * 1.5
+    k = rng.normal(size=(Sk, D)) * 1.5
+    v = rng.normal(size=(Sk, D))
+    qp = np.array([0, 3, 7, 12, 20, -1, 5, 1, 9])
+    kp = rng.permutation(Sk)
+    side = rng.permutation(Sk) < 6          # 6 keys on side a, 8 on side b
+    side[np.argsort(kp)[0]] = True          # key position 0 on side a
+    side[np.argsort(kp)[1]] = False         # key position 1 on side b
+    scale = 0.45
+    for causal in (False, True):
+        parts = []
+        for sel in (side, ~side):
+            vis = (kp[sel][None, :] <= qp[:, None]) if causal else None
+            st = o.ring.absorb_block(o.ring.init_state(Sq, D), q, k[sel], v[sel], scale, vis)
+            parts.append(st)
+        ref_out, ref_lse = o.attention.full_attention(q[None, None], k[None, None],
+                                                      v[None, None], q_pos=qp, k_pos=kp,
+                                                      causal=causal, scale=scale)
+        ref_out, ref_lse = ref_out[0, 0], ref_lse[0, 0]
+        for x, y in ((0, 1), (1, 0)):
+            fo, fl = o.ring.finalize(o.merge.merge_states(parts[x], parts[y]))
+            assert _maxdiff(fo, ref_out) < 1e-12 and _maxdiff(fl, ref_lse) < 1e-12
+            fa, la = o.ring.finalize(parts[x])
+            fb, lb = o.ring.finalize(parts[y])
+            mo, ml = o.merge.merge_outputs(fa, la, fb, lb)
+            assert _maxdiff(mo, ref_out) < 1e-12 and _maxdiff(ml, ref_lse) < 1e-12
+            # merged lse is the library log-sum-exp of the two sides' lse
+            with np.errstate(divide="ignore"):
+                lib = logsumexp(np.stack([la, lb]), axis=0)
+            assert _maxdiff(ml, lib) < 1e-12
+        if causal:
+            assert np.isneginf(ref_lse[5]) and np.all(ref_out[5] == 0)
+            # row at position 0 sees only side a, position 1's row sees both
+            assert np.isneginf(o.ring.finalize(parts[1])[1][0])
+
+
+# ---------------------------------------------------------------------------
+# O3 merge: special cases.  The empty state (m = -inf, l = 0, o = 0) and the
+# empty finalized row (out = 0, lse = -inf) are identities, exactly; two
+# empties stay empty; and merging three parts in either grouping agrees.
+def pin_merge_identities(o):
+    rng = np.random.default_rng(112)
+    R, D = 5, 4
+    q = rng.normal(size=(R, D))
+    k = rng.normal(size=(9, D))
+    v = rng.normal(size=(9, D))
+    st = o.ring.absorb_block(o.ring.init_state(R, D), q, k[:4], v[:4], 0.5)
+    e = o.ring.init_state(R, D)
+    for x, y in ((st, e), (e, st)):
+        m, l, acc = o.merge.merge_states(x, y)
+        assert np.array_equal(m, st[0]) and np.array_equal(l, st[1]) and np.array_equal(acc, st[2])
+    m, l, acc = o.merge.merge_states(e, e)
+    assert np.all(np.isneginf(m)) and np.all(l == 0) and np.all(acc == 0)
+    fo, fl = o.ring.finalize(st)
+    zo, zl = np.zeros((R, D)), np.full(R, -np.inf)
+    for args in ((fo, fl, zo, zl), (zo, zl, fo, fl)):
+        mo, ml = o.merge.merge_outputs(*args)
+        assert np.array_equal(mo, fo) and np.array_equal(ml, fl)
+    mo, ml = o.merge.merge_outputs(zo, zl, zo, zl)
+    assert np.all(mo == 0) and np.all(np.isneginf(ml))
+    # three parts: (a + b) + c == a + (b + c) == ordinary attention
+    parts = [o.ring.absorb_block(o.ring.init_state(R, D), q, k[s], v[s], 0.5)
+             for s in (slice(0, 3), slice(3, 5), slice(5, 9))]
+    left = o.merge.merge_states(o.merge.merge_states(parts[0], parts[1]), parts[2])
+    right = o.merge.merge_states(parts[0], o.merge.merge_states(parts[1], parts[2]))
+    ref = o.attention.full_attention(q[None, None], k[None, None], v[None, None], scale=0.5)
+    for st3 in (left, right):
+        fo3, fl3 = o.ring.finalize(st3)
+        assert _maxdiff(fo3, ref[0][0, 0]) < 1e-12 and _maxdiff(fl3, ref[1][0, 0]) < 1e-12
+    # a dominant side: raising side b's max by 40 makes it the merged max;
+    # side a is scaled by exp(m_a - m), not dropped
+    sb = (parts[1][0] + 40.0, parts[1][1], parts[1][2])
+    mo2 = o.merge.merge_states(parts[0], sb)
+    assert np.all(mo2[0] == sb[0])
+    assert _maxdiff(mo2[1], sb[1] + parts[0][1] * np.exp(parts[0][0] - sb[0])) < 1e-12
+
+
 ALL_PINS = [
     pin_tiny_ring_equals_ordinary,
     pin_library_attention,
@@ -400,4 +490,6 @@ ALL_PINS = [
     pin_layout_maps,
     pin_visit_order,
     pin_initial_max_reading,
+    pin_merge_equals_full,
+    pin_merge_identities,
 ]

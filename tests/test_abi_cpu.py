@@ -41,7 +41,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert n in exported, f"{n} not exported"
         assert getattr(lib, n) is not None
-    assert lib.ra_version() == 100
+    assert lib.ra_version() == 101
 
 
 def dims(B=1, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, dtype=1, scale=0.0):
@@ -130,6 +130,40 @@ def test_workspace_bytes(lib):
     q = 32 * 65536 * 128 * 2
     kv = 8 * 65536 * 128 * 2
     assert ws(d, 8, 1, -1) == 2 * q + 2 * kv + 32 * 65536 * 4
+
+
+def test_merge_errors(lib):
+    M = lib.ra_state_merge
+    a, b = state(), state(m=FAKE + (1 << 20), l=FAKE + (1 << 20) + 4096, acc=FAKE + (2 << 20))
+    r = ctypes.byref
+    expect(M(None, r(b), r(a), None), capi.RA_ERR_NULL, "state")
+    expect(M(r(a), r(b), r(state(Sq=64)), None), capi.RA_ERR_SHAPE, "equal")
+    expect(M(r(a), r(state(D=64)), r(a), None), capi.RA_ERR_SHAPE, "equal")
+    expect(M(r(a), r(b), r(state(D=100)), None), capi.RA_ERR_UNSUPPORTED, "head dim")
+    # out.m on a.l's buffer, out.acc straddling b.acc, out.l == out.m
+    expect(M(r(a), r(b), r(state(m=FAKE + 4096, l=FAKE + (3 << 20), acc=FAKE + (4 << 20))), None),
+           capi.RA_ERR_SHAPE, "overlap")
+    expect(M(r(a), r(b), r(state(m=FAKE + (3 << 20), l=FAKE + (3 << 20) + 4096,
+                                 acc=FAKE + (2 << 20) + 256)), None), capi.RA_ERR_SHAPE, "overlap")
+    expect(M(r(a), r(b), r(state(m=FAKE + (3 << 20), l=FAKE + (3 << 20), acc=FAKE + (4 << 20))), None),
+           capi.RA_ERR_SHAPE, "overlap")
+
+    G = lib.ra_merge
+    oa, la, ob, lb, oo, lo = (FAKE + (i << 20) for i in range(6))
+
+    def g(*args, rows=64, D=128, dtype=1):
+        x = dict(zip(("oa", "la", "ob", "lb", "oo", "lo"), (oa, la, ob, lb, oo, lo)))
+        x.update(dict(args))
+        return G(x["oa"], x["la"], x["ob"], x["lb"], x["oo"], x["lo"], rows, D, dtype, None)
+
+    expect(g(("lb", None)), capi.RA_ERR_NULL, "non-NULL")
+    expect(g(dtype=4), capi.RA_ERR_DTYPE, "dtype")
+    expect(g(rows=0), capi.RA_ERR_SHAPE, "rows")
+    expect(g(D=96), capi.RA_ERR_UNSUPPORTED, "head dim")
+    expect(g(("oo", oo + 4)), capi.RA_ERR_SHAPE, "misaligned")
+    expect(g(("lo", la + 4)), capi.RA_ERR_SHAPE, "overlap")
+    expect(g(("oo", lb)), capi.RA_ERR_SHAPE, "overlap")
+    expect(g(("oo", ob + 64)), capi.RA_ERR_SHAPE, "overlap")
 
 
 def test_permute_and_positions_errors(lib):

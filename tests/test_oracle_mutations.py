@@ -39,6 +39,16 @@ MUTATIONS = [
     ("layouts.py", "(2 * N - 1 - p) * c + (a - c)", "(N + p) * c + (a - c)", "zigzag second chunk"),
     ("layouts.py", "int((keys[None, :] <= qp[:, None]).sum())", "int((keys[None, :] < qp[:, None]).sum())",
      "pair count off by one"),
+    ("merge.py", "l = la * wa + lb * wb", "l = la * wa + lb", "merge drops rescale of l_b"),
+    ("merge.py", "o = oa * wa[..., None] + ob * wb[..., None]", "o = oa * wa[..., None] + ob * wa[..., None]",
+     "merge weights o_b by side a"),
+    ("merge.py", "m = np.maximum(ma, mb)", "m = ma", "merge keeps side a's max"),
+    ("merge.py", "lse = np.where(seen, m + np.log", "lse = np.where(seen, np.log", "merged lse drops max"),
+    ("merge.py", "wb = np.where(seen, _side_weight(lse_b, ref), 0.0)",
+     "wb = np.where(seen, _side_weight(lse_b, m), 0.0)", "merged out weight not normalised"),
+    ("merge.py", "return np.where(finite, np.exp(np.where(finite, x, 0.0) - np.where(finite, ref, 0.0)), 0.0)",
+     "return np.where(finite, np.exp(np.where(finite, x, 0.0) - np.where(finite, ref, 0.0)), 1.0)",
+     "empty side weighted 1"),
 ]
 
 
