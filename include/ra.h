@@ -171,7 +171,8 @@ ra_status ra_state_merge(const ra_state* a, const ra_state* b, const ra_state* o
  * out = out_a e^(lse_a - lse) + out_b e^(lse_b - lse), in out's dtype (round
  * to nearest even for bf16).  A side with lse = -inf contributes nothing; a
  * row empty on both sides gets out = 0, lse = -inf.
- *   out_a, out_b, out: [rows, D] of `dtype`; lse_a, lse_b, lse: [rows] fp32.
+ *   out_a, out_b, out: [rows, D] of `dtype`, 16-byte aligned; lse_a, lse_b,
+ *   lse: [rows] fp32.
  *   out / lse may be exactly out_a / lse_a or out_b / lse_b; other overlaps
  *   are not allowed. */
 ra_status ra_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
