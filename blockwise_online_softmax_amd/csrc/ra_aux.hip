@@ -19,6 +19,16 @@ inline unsigned grid_for(int64_t n) {
   return (unsigned)g;
 }
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin.
+// Renumber them so that each XCD takes one contiguous eighth of the data:
+// per-row values that neighbouring workgroups share (m, l) then sit in one
+// L2 instead of being fetched from HBM by several.
+__device__ inline int64_t xcd_block() {
+  const unsigned b = blockIdx.x, n = gridDim.x;
+  if (n % 8 != 0) return b;
+  return (int64_t)(b % 8) * (n / 8) + b / 8;
+}
+
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
@@ -53,13 +63,12 @@ __global__ void state_init_kernel(float* __restrict__ m, float* __restrict__ l,
 template <int OUT_BF16>
 __global__ void finalize_kernel(const float* __restrict__ m, const float* __restrict__ l,
                                 const float* __restrict__ acc, void* __restrict__ out,
-                                float* __restrict__ lse, int64_t rows, int64_t D) {
+                                float* __restrict__ lse, int64_t rows, int qshift) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t q4 = D / 4;
-  const int64_t n4 = rows * q4;
+  const int64_t n4 = rows << qshift;  // 2^qshift = D / 4 pieces per row
   const f32x4* a4 = reinterpret_cast<const f32x4*>(acc);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const int64_t row = i / q4;
+  for (int64_t i = xcd_block() * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const int64_t row = i >> qshift;
     const float lv = l[row];
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     if (lv > 0.f) {
@@ -72,7 +81,7 @@ __global__ void finalize_kernel(const float* __restrict__ m, const float* __rest
     } else {
       __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out) + i);
     }
-    if (lse != nullptr && (i - row * q4) == 0)
+    if (lse != nullptr && (i & ((1 << qshift) - 1)) == 0)
       lse[row] = lv > 0.f ? m[row] + logf(lv) : -__builtin_inff();
   }
 }
@@ -127,10 +136,12 @@ hipError_t launch_state_init(float* m, float* l, float* acc, int64_t rows, int64
 hipError_t launch_finalize(const float* m, const float* l, const float* acc, void* out,
                            float* lse, int64_t rows, int64_t D, int out_dtype, hipStream_t s) {
   const dim3 g(grid_for(rows * D / 4));
+  int qs = 0;  // D is a power of two from 8 to 128
+  while (((int64_t)4 << qs) < D) ++qs;
   if (out_dtype == RA_BF16)
-    hipLaunchKernelGGL(finalize_kernel<1>, g, dim3(kThreads), 0, s, m, l, acc, out, lse, rows, D);
+    hipLaunchKernelGGL(finalize_kernel<1>, g, dim3(kThreads), 0, s, m, l, acc, out, lse, rows, qs);
   else
-    hipLaunchKernelGGL(finalize_kernel<0>, g, dim3(kThreads), 0, s, m, l, acc, out, lse, rows, D);
+    hipLaunchKernelGGL(finalize_kernel<0>, g, dim3(kThreads), 0, s, m, l, acc, out, lse, rows, qs);
   return hipGetLastError();
 }
 

@@ -34,6 +34,16 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kThreads = 256;
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin.
+// Renumber them so that each XCD takes one contiguous eighth of the rows:
+// the per-row m / l / lse values that neighbouring workgroups share then sit
+// in one L2 instead of being fetched from HBM by several.
+__device__ inline int64_t xcd_block() {
+  const unsigned b = blockIdx.x, n = gridDim.x;
+  if (n % 8 != 0) return b;
+  return (int64_t)(b % 8) * (n / 8) + b / 8;
+}
+
 __device__ inline unsigned pack_bf16x2(float a, float b) {
   f32x2 v = {a, b};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
@@ -63,7 +73,7 @@ __global__ void state_merge_kernel(const float* ma, const float* la, const float
                                    float* mo, float* lo, float* acco, int64_t pieces, int pshift) {
 #pragma clang fp contract(off)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += stride) {
+  for (int64_t i = xcd_block() * blockDim.x + threadIdx.x; i < pieces; i += stride) {
     const int64_t row = i >> pshift;
     float m, wa, wb;
     side_weights(ma[row], mb[row], m, wa, wb);
@@ -84,7 +94,7 @@ __global__ void out_merge_kernel(const void* oa, const float* lsea, const void* 
                                  int pshift) {
 #pragma clang fp contract(off)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += stride) {
+  for (int64_t i = xcd_block() * blockDim.x + threadIdx.x; i < pieces; i += stride) {
     const int64_t row = i >> pshift;
     float x, wa, wb;
     side_weights(lsea[row], lseb[row], x, wa, wb);
