@@ -53,6 +53,7 @@ struct AttnParams {
   int layout, N, blk;  // POS_ANALYTIC
   float scale;     // score scale
   float sl2;       // scale * log2(e)
+  int redo;        // 1: only redo work items whose lse holds a NaN mark
 };
 
 // Launchers (return hipGetLastError() after the launch).

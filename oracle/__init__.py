@@ -26,6 +26,8 @@ Modules:
              the causal pair count per device.
   merge      O3: merge of two partial results over disjoint key sets, as
              running states (m, l, o) or as finalized (out, lse).
+  vocab_ce   O4: vocab-parallel cross-entropy (the page's three shard steps),
+             the plain per-row definition and the gradient.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, printed page values, library routines, brute force).  What no
@@ -42,6 +44,7 @@ from .ring import (  # noqa: F401
     ring_attention,
 )
 from .merge import merge_states, merge_outputs  # noqa: F401
+from . import vocab_ce  # noqa: F401
 from .layouts import (  # noqa: F401
     LAYOUTS,
     device_positions,

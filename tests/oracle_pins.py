@@ -12,7 +12,9 @@ Sources (page titles and sections):
   [DT2]  "3.6 Distributed Training II ...": "Ring Attention",
          "Vocab-parallel cross-entropy".
   O3 (merge) follows [M23] "The Math" (the fold ignores block order) and
-  [DT2] "Vocab-parallel cross-entropy" (max, then sum of rescaled Z).
+  [DT2] "Vocab-parallel cross-entropy" (max, then sum of rescaled Z); O4
+  (vocab-parallel cross-entropy) follows [DT2] "Vocab-parallel
+  cross-entropy".
 """
 
 import json
@@ -474,6 +476,72 @@ def pin_merge_identities(o):
     assert _maxdiff(mo2[1], sb[1] + parts[0][1] * np.exp(parts[0][0] - sb[0])) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# O4 vocab-parallel cross-entropy ([DT2] "Vocab-parallel cross-entropy").
+# The page's three-step shard algorithm and the plain per-row definition
+# against torch's fp64 cross_entropy, for several shard counts, with targets
+# on shard boundaries, and the gradient against torch autograd.
+def pin_vocab_ce_library(o):
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(121)
+    N, V = 37, 48
+    z = rng.normal(size=(N, V)) * 3.0
+    tg = rng.integers(0, V, size=N)
+    tg[:6] = [0, 6, 12, 23, 24, 47]          # first / last columns of shards
+    ref = F.cross_entropy(torch.from_numpy(z), torch.from_numpy(tg), reduction="none").numpy()
+    assert _maxdiff(o.vocab_ce.cross_entropy_rows(z, tg), ref) < 1e-12
+    for t in (1, 2, 4, 8):
+        loss, mean, lse = o.vocab_ce.vocab_parallel(z, tg, t)
+        assert _maxdiff(loss, ref) < 1e-12, t
+        assert abs(mean - ref.mean()) < 1e-12
+        from scipy.special import logsumexp
+        assert _maxdiff(lse, logsumexp(z, axis=1)) < 1e-12
+    # gradient of the mean loss
+    zt = torch.from_numpy(z).requires_grad_(True)
+    F.cross_entropy(zt, torch.from_numpy(tg)).backward()
+    assert _maxdiff(o.vocab_ce.ce_grad(z, tg, 1.0 / N), zt.grad.numpy()) < 1e-12
+
+
+# O4 closed forms and brute force: uniform logits give log V; a dominant
+# target gives ~0; a target outside the vocab gives the bare log-sum-exp; one
+# shard's statistics against pure-Python loops with math.exp.
+def pin_vocab_ce_closed_forms(o):
+    N, V = 4, 24
+    z = np.zeros((N, V))
+    for t in (1, 3):
+        loss, mean, _ = o.vocab_ce.vocab_parallel(z, np.array([0, 5, 23, 11]), t)
+        assert _maxdiff(loss, np.full(N, math.log(V))) < 1e-12
+    zd = np.zeros((2, V))
+    zd[0, 7] = 40.0
+    zd[1, 7] = 40.0
+    loss, _, _ = o.vocab_ce.vocab_parallel(zd, np.array([7, 8]), 4)
+    assert abs(loss[0] - math.log1p((V - 1) * math.exp(-40.0))) < 1e-15
+    assert abs(loss[1] - (40.0 + math.log1p((V - 1) * math.exp(-40.0)))) < 1e-12
+    rng = np.random.default_rng(122)
+    zr = rng.normal(size=(3, V))
+    loss, _, lse = o.vocab_ce.vocab_parallel(zr, np.array([-1, V, 2]), 2)
+    assert abs(loss[0] - lse[0]) < 1e-15 and abs(loss[1] - lse[1]) < 1e-15
+    assert abs(loss[2] - (lse[2] - zr[2, 2])) < 1e-12
+    # one shard, brute force
+    start, V_loc = 8, 8
+    tg = np.array([9, 3, 15])
+    m, s, pred = o.vocab_ce.shard_stats(zr[:, start:start + V_loc], tg, start)
+    for r in range(3):
+        row = [float(x) for x in zr[r, start:start + V_loc]]
+        mx = max(row)
+        assert m[r] == mx
+        assert abs(s[r] - sum(math.exp(x - mx) for x in row)) < 1e-12
+        want = row[tg[r] - start] if start <= tg[r] < start + V_loc else 0.0
+        assert pred[r] == want
+    # gradient rows sum to zero; the target entry is softmax - 1
+    g = o.vocab_ce.ce_grad(zr, np.array([0, 5, 2]), 1.0)
+    assert _maxdiff(g.sum(axis=1), np.zeros(3)) < 1e-12
+    from scipy.special import softmax
+    assert abs(g[1, 5] - (softmax(zr[1])[5] - 1.0)) < 1e-12
+
+
 ALL_PINS = [
     pin_tiny_ring_equals_ordinary,
     pin_library_attention,
@@ -492,4 +560,6 @@ ALL_PINS = [
     pin_initial_max_reading,
     pin_merge_equals_full,
     pin_merge_identities,
+    pin_vocab_ce_library,
+    pin_vocab_ce_closed_forms,
 ]

@@ -49,6 +49,18 @@ MUTATIONS = [
     ("merge.py", "return np.where(finite, np.exp(np.where(finite, x, 0.0) - np.where(finite, ref, 0.0)), 0.0)",
      "return np.where(finite, np.exp(np.where(finite, x, 0.0) - np.where(finite, ref, 0.0)), 1.0)",
      "empty side weighted 1"),
+    ("vocab_ce.py", "loss = np.log(Z) + m - pred", "loss = np.log(Z) - pred", "vocab loss drops max"),
+    ("vocab_ce.py", "own = (tg >= start) & (tg < start + V_loc)\n        local",
+     "own = (tg >= start) & (tg <= start + V_loc)\n        local", "vocab shard owns next shard's first id"),
+    ("vocab_ce.py", "Z = np.sum(np.stack([np.exp(sh - m[:, None])", "Z = np.sum(np.stack([np.exp(sh)",
+     "vocab sum not shifted by max"),
+    ("vocab_ce.py", "g[np.arange(N)[own], tg[own]] -= 1.0", "g[np.arange(N)[own], tg[own]] += 1.0",
+     "gradient one-hot sign"),
+    ("vocab_ce.py", "    return g * scale", "    return g", "gradient scale dropped"),
+    ("vocab_ce.py", "return logsumexp(z, axis=1) - zt", "return logsumexp(z, axis=1) + zt",
+     "per-row loss target sign"),
+    ("vocab_ce.py", "    m = z.max(axis=1)\n    s = np.exp", "    m = z.mean(axis=1)\n    s = np.exp",
+     "shard max replaced by mean"),
 ]
 
 
