@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--merge", action="store_true",
                     help="ra_merge and ra_state_merge on the rows of the 32K-token x 32-head "
                          "x D=128 query set (HBM GB/s); one JSON line each")
+    ap.add_argument("--vocab-ce", action="store_true",
+                    help="vocab-parallel cross-entropy forward and gradient on 8192 rows x 128,256 "
+                         "bf16 logits over 8 shards (HBM GB/s); one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (contiguous ra_permute) so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -356,6 +359,48 @@ def merge_bench(args):
         "steps": args.steps, "data": "synthetic"}), flush=True)
 
 
+def vocab_ce_bench(args):
+    """Vocab-parallel cross-entropy on 8192 rows of bf16 logits over a
+    128,256-entry vocabulary (Llama-3's) split into 8 shards: the forward
+    (shard statistics + combine + mean) and the gradient of the mean loss.
+    Bytes are algorithmic: the forward reads the logits once (plus targets
+    and the [8, N] statistics), the gradient reads them and writes the
+    gradient once."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+
+    N, V, t = 8192, 128256, 8
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(88)
+    z = (torch.randn((N, V), generator=g, device="cuda") * 3.0).to(torch.bfloat16)
+    tg = torch.randint(0, V, (N,), generator=g, device="cuda", dtype=torch.int64)
+    loss = torch.empty(N, dtype=torch.float32, device="cuda")
+    lse = torch.empty(N, dtype=torch.float32, device="cuda")
+    mean = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ra.ra_vocab_ce_workspace_bytes(N, t), dtype=torch.uint8, device="cuda")
+    grad = torch.empty_like(z)
+    ms = timed(lambda: ra.ra_vocab_ce(z, tg, t, loss, mean, lse, ws, stream=stream), args.steps,
+               args.warmup, stream)
+    nbytes = N * V * 2 + N * 8 + 3 * t * N * 4 * 2 + N * 8
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "ra_vocab_ce forward HBM GB/s (bf16 logits, 8 shards)", "rows": N, "vocab": V,
+        "shards": t, "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+        "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "steps": args.steps, "data": "synthetic"}), flush=True)
+    ms = timed(lambda: ra.ra_vocab_ce_grad(z, tg, lse, 0, 1.0 / N, grad, stream=stream),
+               args.steps, args.warmup, stream)
+    nbytes = 2 * N * V * 2 + N * 12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "ra_vocab_ce_grad HBM GB/s (bf16 logits and gradient)", "rows": N, "vocab": V,
+        "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+        "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "steps": args.steps, "data": "synthetic"}), flush=True)
+
+
 def tiny_latency(args):
     """The pages' tiny case (4 devices x 3 tokens, d = 8, fp32, non-causal):
     microseconds per ra_ring call, HIP events on the launch stream."""
@@ -403,6 +448,9 @@ def main():
         return
     if args.merge:
         merge_bench(args)
+        return
+    if args.vocab_ce:
+        vocab_ce_bench(args)
         return
     wkey, layout, device = WORKLOADS[args.workload]
     cfg = workloads.WORKLOADS[wkey]

@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libra.so")
 
-SOURCES = ["ra_api.cpp", "ra_aux.hip", "ra_attn_valu.hip", "ra_attn_mfma.hip", "ra_merge.hip"]
+SOURCES = ["ra_api.cpp", "ra_aux.hip", "ra_attn_valu.hip", "ra_attn_mfma.hip", "ra_merge.hip",
+           "ra_vocab_ce.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -36,7 +36,8 @@ LAYOUT_IDS = {"contiguous": RA_CONTIGUOUS, "striped": RA_STRIPED, "zigzag": RA_Z
 
 EXPORTED = ["ra_state_init", "ra_block_step", "ra_finalize", "ra_ring",
             "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_state_merge",
-            "ra_merge", "ra_last_error", "ra_version"]
+            "ra_merge", "ra_vocab_ce_shard", "ra_vocab_ce_combine", "ra_vocab_ce_grad",
+            "ra_vocab_ce_workspace_bytes", "ra_vocab_ce", "ra_last_error", "ra_version"]
 
 
 class RaDims(ctypes.Structure):
@@ -78,6 +79,12 @@ def load(path=None):
         "ra_positions": (i32, [vp, i64, i32, i32, i32, vp]),
         "ra_state_merge": (i32, [state_p, state_p, state_p, vp]),
         "ra_merge": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
+        "ra_vocab_ce_shard": (i32, [vp, i64, vp, i64, i64, i64, i32, vp, vp, vp, vp]),
+        "ra_vocab_ce_combine": (i32, [vp, vp, vp, i32, i64, vp, vp, vp]),
+        "ra_vocab_ce_grad": (i32, [vp, i64, vp, vp, i64, i64, i64, ctypes.c_float, i32, vp, i64,
+                                   vp]),
+        "ra_vocab_ce_workspace_bytes": (sz, [i64, i32]),
+        "ra_vocab_ce": (i32, [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]),
         "ra_last_error": (ctypes.c_char_p, []),
         "ra_version": (i32, []),
     }
@@ -262,6 +269,81 @@ def ra_merge(out_a, lse_a, out_b, lse_b, out, lse, stream=None):
             raise ValueError(f"{n} has {t.numel()} elements, expected {rows}")
     _check(load().ra_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out),
                            _ptr(lse), rows, D, _dtype_id(out_a), _stream(stream)), "ra_merge")
+
+
+def _row_stride(t):
+    """Row stride (elements) of a 2-D tensor whose rows are dense."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("logits / grad must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def ra_vocab_ce_shard(logits, target, vocab_start, m, z_sum, pred, stream=None):
+    """One vocab shard's row statistics.  logits: [N, V_loc] (a column slice
+    of a larger matrix is fine); target: [N] int64 global ids."""
+    torch = _torch()
+    if not logits.is_cuda:
+        raise ValueError("logits must be on the GPU")
+    _require(target, "target", torch.int64)
+    for t, n in ((m, "m"), (z_sum, "z_sum"), (pred, "pred")):
+        _require(t, n, torch.float32)
+    N, V_loc = logits.shape
+    _check(load().ra_vocab_ce_shard(_ptr(logits), _row_stride(logits), _ptr(target), N, V_loc,
+                                    int(vocab_start), _dtype_id(logits), _ptr(m), _ptr(z_sum),
+                                    _ptr(pred), _stream(stream)), "ra_vocab_ce_shard")
+
+
+def ra_vocab_ce_combine(m, z_sum, pred, loss, lse=None, stream=None):
+    """Combine [t, N] shard statistics into per-row loss (and lse)."""
+    torch = _torch()
+    for t, n in ((m, "m"), (z_sum, "z_sum"), (pred, "pred"), (loss, "loss")):
+        _require(t, n, torch.float32)
+    if lse is not None:
+        _require(lse, "lse", torch.float32)
+    t, N = m.shape
+    _check(load().ra_vocab_ce_combine(_ptr(m), _ptr(z_sum), _ptr(pred), t, N, _ptr(loss),
+                                      _ptr(lse), _stream(stream)), "ra_vocab_ce_combine")
+
+
+def ra_vocab_ce_grad(logits, target, lse, vocab_start, scale, grad, stream=None):
+    """grad = scale * (exp(logits - lse) - onehot) for one shard."""
+    torch = _torch()
+    if not logits.is_cuda or not grad.is_cuda:
+        raise ValueError("logits and grad must be on the GPU")
+    if grad.dtype != logits.dtype or grad.shape != logits.shape:
+        raise ValueError("grad must match the logits' shape and dtype")
+    _require(target, "target", torch.int64)
+    _require(lse, "lse", torch.float32)
+    N, V_loc = logits.shape
+    _check(load().ra_vocab_ce_grad(_ptr(logits), _row_stride(logits), _ptr(target), _ptr(lse), N,
+                                   V_loc, int(vocab_start), float(scale), _dtype_id(logits),
+                                   _ptr(grad), _row_stride(grad), _stream(stream)),
+           "ra_vocab_ce_grad")
+
+
+def ra_vocab_ce_workspace_bytes(N, t):
+    n = load().ra_vocab_ce_workspace_bytes(int(N), int(t))
+    if n == ctypes.c_size_t(-1).value:
+        raise RuntimeError(f"ra_vocab_ce_workspace_bytes: {last_error()}")
+    return int(n)
+
+
+def ra_vocab_ce(logits, target, t, loss, mean_loss, lse=None, ws=None, stream=None):
+    """Whole vocab-parallel cross-entropy over t shards of logits [N, V]."""
+    torch = _torch()
+    _require(logits, "logits")
+    _require(target, "target", torch.int64)
+    _require(loss, "loss", torch.float32)
+    _require(mean_loss, "mean_loss", torch.float32)
+    if lse is not None:
+        _require(lse, "lse", torch.float32)
+    N, V = logits.shape
+    if ws is None:
+        ws = torch.empty(ra_vocab_ce_workspace_bytes(N, t), dtype=torch.uint8,
+                         device=logits.device)
+    _check(load().ra_vocab_ce(_ptr(logits), _ptr(target), N, V, int(t), _dtype_id(logits),
+                              _ptr(loss), _ptr(mean_loss), _ptr(lse), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "ra_vocab_ce")
 
 
 def ra_version():

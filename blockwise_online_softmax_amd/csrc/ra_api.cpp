@@ -145,7 +145,7 @@ hipError_t launch_attention(const ra::AttnParams& p, int D, int dtype, bool caus
 
 extern "C" {
 
-int ra_version(void) { return 101; }
+int ra_version(void) { return 102; }
 
 const char* ra_last_error(void) { return g_err; }
 
@@ -285,6 +285,134 @@ ra_status ra_merge(const void* out_a, const float* lse_a, const void* out_b, con
   ra_status s = hip_status(ra::launch_out_merge(out_a, lse_a, out_b, lse_b, out, lse, rows, D,
                                                 dtype, (hipStream_t)stream),
                            "ra_merge launch");
+  return s == RA_OK ? ok() : s;
+}
+
+namespace {
+
+constexpr int kMaxShards = 1024;
+
+ra_status check_ce_rows(const void* logits, int64_t ld, const int64_t* target, int64_t N,
+                        int64_t V_loc, ra_dtype dtype) {
+  if (logits == nullptr || target == nullptr)
+    return fail(RA_ERR_NULL, "logits and target must be non-NULL");
+  if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (N < 1 || N >= kMaxSeq) return fail(RA_ERR_SHAPE, "N must be in [1, 2^31)");
+  if (V_loc < 1 || V_loc >= ((int64_t)1 << 40)) return fail(RA_ERR_SHAPE, "V_loc out of range");
+  if (ld < V_loc) return fail(RA_ERR_SHAPE, "row stride ld must be >= V_loc");
+  if (!aligned(logits, dtype == RA_BF16 ? 2 : 4) || !aligned(target, 8))
+    return fail(RA_ERR_SHAPE, "logits / target misaligned");
+  return RA_OK;
+}
+
+struct CeWorkspace {
+  int64_t stats, partial, total;  // byte offsets
+};
+CeWorkspace ce_workspace(int64_t N, int t) {
+  CeWorkspace w;
+  w.stats = 0;
+  w.partial = round256(3 * (int64_t)t * N * 4);
+  w.total = w.partial + round256(ra::ce_partial_count(N) * 4);
+  return w;
+}
+
+}  // namespace
+
+ra_status ra_vocab_ce_shard(const void* logits, int64_t ld, const int64_t* target, int64_t N,
+                            int64_t V_loc, int64_t vocab_start, ra_dtype dtype, float* m,
+                            float* z_sum, float* pred, void* stream) {
+  ra_status s = check_ce_rows(logits, ld, target, N, V_loc, dtype);
+  if (s != RA_OK) return s;
+  if (m == nullptr || z_sum == nullptr || pred == nullptr)
+    return fail(RA_ERR_NULL, "m, z_sum and pred must be non-NULL");
+  if (!aligned(m, 4) || !aligned(z_sum, 4) || !aligned(pred, 4))
+    return fail(RA_ERR_SHAPE, "m / z_sum / pred misaligned");
+  (void)hipGetLastError();
+  s = hip_status(ra::launch_ce_stats(logits, ld, target, N, V_loc, vocab_start, 1, dtype, m, z_sum,
+                                     pred, (hipStream_t)stream),
+                 "ra_vocab_ce_shard launch");
+  return s == RA_OK ? ok() : s;
+}
+
+ra_status ra_vocab_ce_combine(const float* m, const float* z_sum, const float* pred, int t,
+                              int64_t N, float* loss, float* lse, void* stream) {
+  if (m == nullptr || z_sum == nullptr || pred == nullptr || loss == nullptr)
+    return fail(RA_ERR_NULL, "m, z_sum, pred and loss must be non-NULL");
+  if (t < 1 || t > kMaxShards) return fail(RA_ERR_SHAPE, "t must be in [1, %d]", kMaxShards);
+  if (N < 1 || N >= kMaxSeq) return fail(RA_ERR_SHAPE, "N must be in [1, 2^31)");
+  if (!aligned(m, 4) || !aligned(z_sum, 4) || !aligned(pred, 4) || !aligned(loss, 4) ||
+      (lse != nullptr && !aligned(lse, 4)))
+    return fail(RA_ERR_SHAPE, "buffers misaligned");
+  (void)hipGetLastError();
+  ra_status s = hip_status(ra::launch_ce_combine(m, z_sum, pred, t, N, loss, lse, nullptr, nullptr,
+                                                 (hipStream_t)stream),
+                           "ra_vocab_ce_combine launch");
+  return s == RA_OK ? ok() : s;
+}
+
+ra_status ra_vocab_ce_grad(const void* logits, int64_t ld, const int64_t* target, const float* lse,
+                           int64_t N, int64_t V_loc, int64_t vocab_start, float scale,
+                           ra_dtype dtype, void* grad, int64_t ldg, void* stream) {
+  ra_status s = check_ce_rows(logits, ld, target, N, V_loc, dtype);
+  if (s != RA_OK) return s;
+  if (lse == nullptr || grad == nullptr) return fail(RA_ERR_NULL, "lse and grad must be non-NULL");
+  if (ldg < V_loc) return fail(RA_ERR_SHAPE, "row stride ldg must be >= V_loc");
+  if (!aligned(lse, 4) || !aligned(grad, dtype == RA_BF16 ? 2 : 4))
+    return fail(RA_ERR_SHAPE, "lse / grad misaligned");
+  if (!std::isfinite(scale)) return fail(RA_ERR_SHAPE, "scale must be finite");
+  const int64_t es = dtype == RA_BF16 ? 2 : 4;
+  if (N * ((V_loc * es + 4095) / 4096) >= kMaxSeq)
+    return fail(RA_ERR_SHAPE, "N x V_loc too large for one launch (split the rows)");
+  const uintptr_t g0 = (uintptr_t)grad, g1 = g0 + (uintptr_t)(((N - 1) * ldg + V_loc) * es);
+  const uintptr_t l0 = (uintptr_t)logits, l1 = l0 + (uintptr_t)(((N - 1) * ld + V_loc) * es);
+  if (g0 < l1 && l0 < g1) return fail(RA_ERR_SHAPE, "grad overlaps the logits");
+  (void)hipGetLastError();
+  s = hip_status(ra::launch_ce_grad(logits, ld, target, lse, N, V_loc, vocab_start, 1, scale,
+                                    dtype, grad, ldg, (hipStream_t)stream),
+                 "ra_vocab_ce_grad launch");
+  return s == RA_OK ? ok() : s;
+}
+
+size_t ra_vocab_ce_workspace_bytes(int64_t N, int t) {
+  if (N < 1 || N >= kMaxSeq || t < 1 || t > kMaxShards) {
+    fail(RA_ERR_SHAPE, "N must be in [1, 2^31) and t in [1, %d]", kMaxShards);
+    return (size_t)-1;
+  }
+  ok();
+  return (size_t)ce_workspace(N, t).total;
+}
+
+ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int64_t V, int t,
+                      ra_dtype dtype, float* loss, float* mean_loss, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (t < 1 || t > kMaxShards) return fail(RA_ERR_SHAPE, "t must be in [1, %d]", kMaxShards);
+  if (V < 1 || V % t != 0) return fail(RA_ERR_SHAPE, "V must be a positive multiple of t");
+  ra_status s = check_ce_rows(logits, V, target, N, V / t, dtype);
+  if (s != RA_OK) return s;
+  if (loss == nullptr || mean_loss == nullptr)
+    return fail(RA_ERR_NULL, "loss and mean_loss must be non-NULL");
+  if (!aligned(loss, 4) || !aligned(mean_loss, 4) || (lse != nullptr && !aligned(lse, 4)))
+    return fail(RA_ERR_SHAPE, "loss / mean_loss / lse misaligned");
+  const CeWorkspace w = ce_workspace(N, t);
+  if (ws == nullptr) return fail(RA_ERR_WORKSPACE, "workspace required (%lld bytes)", (long long)w.total);
+  if ((int64_t)ws_bytes < w.total)
+    return fail(RA_ERR_WORKSPACE, "workspace too small: %zu < %lld", ws_bytes, (long long)w.total);
+  if (!aligned(ws, 256)) return fail(RA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  float* st = reinterpret_cast<float*>(base + w.stats);
+  float* partial = reinterpret_cast<float*>(base + w.partial);
+  const int64_t V_loc = V / t;
+  float* m = st;
+  float* zs = st + (int64_t)t * N;
+  float* pr = st + 2 * (int64_t)t * N;
+  (void)hipGetLastError();
+  s = hip_status(ra::launch_ce_stats(logits, V, target, N, V_loc, 0, t, dtype, m, zs, pr,
+                                     (hipStream_t)stream),
+                 "ra_vocab_ce shard launch");
+  if (s != RA_OK) return s;
+  s = hip_status(ra::launch_ce_combine(m, zs, pr, t, N, loss, lse, partial, mean_loss,
+                                       (hipStream_t)stream),
+                 "ra_vocab_ce combine launch");
   return s == RA_OK ? ok() : s;
 }
 

@@ -53,7 +53,6 @@ struct AttnParams {
   int layout, N, blk;  // POS_ANALYTIC
   float scale;     // score scale
   float sl2;       // scale * log2(e)
-  int redo;        // 1: only redo work items whose lse holds a NaN mark
 };
 
 // Launchers (return hipGetLastError() after the launch).
@@ -73,6 +72,15 @@ hipError_t launch_positions(int32_t* pos, int64_t S, int N, int layout, int devi
 hipError_t launch_state_merge(const float* ma, const float* la, const float* acca,
                               const float* mb, const float* lb, const float* accb, float* mo,
                               float* lo, float* acco, int64_t rows, int64_t D, hipStream_t s);
+hipError_t launch_ce_stats(const void* logits, int64_t ld, const int64_t* target, int64_t N,
+                           int64_t V_loc, int64_t start0, int t, int dtype, float* m, float* s,
+                           float* p, hipStream_t st);
+int64_t ce_partial_count(int64_t N);
+hipError_t launch_ce_combine(const float* m, const float* s, const float* p, int t, int64_t N,
+                             float* loss, float* lse, float* partial, float* mean, hipStream_t st);
+hipError_t launch_ce_grad(const void* logits, int64_t ld, const int64_t* target, const float* lse,
+                          int64_t N, int64_t V_loc, int64_t start0, int t, float scale, int dtype,
+                          void* grad, int64_t ldg, hipStream_t st);
 hipError_t launch_out_merge(const void* oa, const float* lsea, const void* ob, const float* lseb,
                             void* oo, float* lseo, int64_t rows, int64_t D, int dtype,
                             hipStream_t s);

@@ -178,6 +178,56 @@ ra_status ra_state_merge(const ra_state* a, const ra_state* b, const ra_state* o
 ra_status ra_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
                    void* out, float* lse, int64_t rows, int64_t D, ra_dtype dtype, void* stream);
 
+/* ---- Vocab-parallel cross-entropy ("3.6 Distributed Training II",
+ * "Vocab-parallel cross-entropy"): the loss of a row of logits z with global
+ * target id t is logsumexp(z) - z[t].  With the vocab split into shards, each
+ * shard reduces its columns to a row max, a sum of exponentials and the
+ * target logit if it owns t; a MAX and two SUMs over the shards combine
+ * them; the gradient softmax(z) - onehot(t) is split like the logits.
+ * Logits are bf16 or fp32 (computed in fp32); targets are int64 ids; a target
+ * outside the vocab is owned by no shard (its target logit counts as 0). */
+
+/* One shard's statistics, in a single pass over its logits: for each row r
+ * of the shard's logits [N, V_loc] (row stride ld elements, element-aligned),
+ *   m[r]     = max_j z[r][j],
+ *   z_sum[r] = sum_j exp(z[r][j] - m[r])   (against the shard's own max),
+ *   pred[r]  = z[r][target[r] - vocab_start] if the shard owns target[r]
+ *              (vocab_start <= target[r] < vocab_start + V_loc), else 0.
+ * A row of -inf logits gives m = -inf, z_sum = 0.  m, z_sum, pred: [N] fp32;
+ * target: [N].  N < 2^31. */
+ra_status ra_vocab_ce_shard(const void* logits, int64_t ld, const int64_t* target, int64_t N,
+                            int64_t V_loc, int64_t vocab_start, ra_dtype dtype, float* m,
+                            float* z_sum, float* pred, void* stream);
+
+/* Combine the statistics of t shards ([t, N] each, shard k's rows at k*N):
+ * M = max_k m_k, Z = sum_k z_sum_k exp(m_k - M), P = sum_k pred_k;
+ * loss[r] = M + log Z - P and, unless lse is NULL, lse[r] = M + log Z. */
+ra_status ra_vocab_ce_combine(const float* m, const float* z_sum, const float* pred, int t,
+                              int64_t N, float* loss, float* lse, void* stream);
+
+/* Gradient of scale x (the sum of the row losses) with respect to one shard's
+ * logits: grad[r][j] = scale * (exp(z[r][j] - lse[r]) - [j == target[r] -
+ * vocab_start]), written in `dtype` (bf16 rounded to nearest even) with row
+ * stride ldg.  lse from ra_vocab_ce_combine / ra_vocab_ce; scale = 1/N gives
+ * the gradient of the mean loss.  grad must not overlap the logits.
+ * N x ceil(V_loc x element size / 4096) < 2^31. */
+ra_status ra_vocab_ce_grad(const void* logits, int64_t ld, const int64_t* target, const float* lse,
+                           int64_t N, int64_t V_loc, int64_t vocab_start, float scale,
+                           ra_dtype dtype, void* grad, int64_t ldg, void* stream);
+
+/* Bytes of workspace ra_vocab_ce needs for N rows and t shards. */
+size_t ra_vocab_ce_workspace_bytes(int64_t N, int t);
+
+/* The whole vocab-parallel cross-entropy on one GPU: logits [N, V] (dense
+ * rows) split into t shards of V/t columns (V % t == 0, 1 <= t <= 1024), each
+ * reduced by the shard kernel, then combined.  loss: [N] fp32; mean_loss: one
+ * fp32 (device), the mean of loss summed in a fixed order (deterministic);
+ * lse: [N] fp32 or NULL.  ws: at least ra_vocab_ce_workspace_bytes(N, t)
+ * bytes, 256-byte aligned. */
+ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int64_t V, int t,
+                      ra_dtype dtype, float* loss, float* mean_loss, float* lse, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);
 

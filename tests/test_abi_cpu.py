@@ -41,7 +41,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert n in exported, f"{n} not exported"
         assert getattr(lib, n) is not None
-    assert lib.ra_version() == 101
+    assert lib.ra_version() == 102
 
 
 def dims(B=1, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, dtype=1, scale=0.0):
@@ -164,6 +164,40 @@ def test_merge_errors(lib):
     expect(g(("lo", la + 4)), capi.RA_ERR_SHAPE, "overlap")
     expect(g(("oo", lb)), capi.RA_ERR_SHAPE, "overlap")
     expect(g(("oo", ob + 64)), capi.RA_ERR_SHAPE, "overlap")
+
+
+def test_vocab_ce_errors(lib):
+    S = lib.ra_vocab_ce_shard
+    L, T = FAKE, FAKE + (1 << 20)
+    outs = (FAKE + (2 << 20), FAKE + (3 << 20), FAKE + (4 << 20))
+    expect(S(None, 16, T, 4, 16, 0, 1, *outs, None), capi.RA_ERR_NULL, "logits")
+    expect(S(L, 16, T, 4, 16, 0, 7, *outs, None), capi.RA_ERR_DTYPE, "dtype")
+    expect(S(L, 16, T, 0, 16, 0, 1, *outs, None), capi.RA_ERR_SHAPE, "N must")
+    expect(S(L, 8, T, 4, 16, 0, 1, *outs, None), capi.RA_ERR_SHAPE, "ld")
+    expect(S(L + 1, 16, T, 4, 16, 0, 1, *outs, None), capi.RA_ERR_SHAPE, "misaligned")
+    expect(S(L, 16, T + 4, 4, 16, 0, 1, *outs, None), capi.RA_ERR_SHAPE, "misaligned")
+    expect(S(L, 16, T, 4, 16, 0, 1, None, outs[1], outs[2], None), capi.RA_ERR_NULL, "z_sum")
+    C = lib.ra_vocab_ce_combine
+    expect(C(*outs, 0, 4, FAKE, None, None), capi.RA_ERR_SHAPE, "t must")
+    expect(C(*outs, 2, 4, None, None, None), capi.RA_ERR_NULL, "loss")
+    G = lib.ra_vocab_ce_grad
+    lse, grad = FAKE + (5 << 20), FAKE + (6 << 20)
+    expect(G(L, 16, T, None, 4, 16, 0, 1.0, 1, grad, 16, None), capi.RA_ERR_NULL, "lse")
+    expect(G(L, 16, T, lse, 4, 16, 0, float("inf"), 1, grad, 16, None), capi.RA_ERR_SHAPE, "finite")
+    expect(G(L, 16, T, lse, 4, 16, 0, 1.0, 1, L + 32, 16, None), capi.RA_ERR_SHAPE, "overlap")
+    expect(G(L, 16, T, lse, 4, 16, 0, 1.0, 1, grad, 8, None), capi.RA_ERR_SHAPE, "ldg")
+    W = lib.ra_vocab_ce_workspace_bytes
+    assert W(8192, 8) == 256 * ((3 * 8 * 8192 * 4 + 255) // 256) + 256 * ((128 * 4 + 255) // 256)
+    assert W(0, 8) == ctypes.c_size_t(-1).value and "N must" in capi.last_error()
+    need = W(4, 2)
+    V = lib.ra_vocab_ce
+    ws = FAKE + (8 << 20)
+    expect(V(L, T, 4, 15, 2, 1, FAKE, FAKE, None, ws, need, None), capi.RA_ERR_SHAPE, "multiple")
+    expect(V(L, T, 4, 16, 0, 1, FAKE, FAKE, None, ws, need, None), capi.RA_ERR_SHAPE, "t must")
+    expect(V(L, T, 4, 16, 2, 1, FAKE, FAKE, None, None, 0, None), capi.RA_ERR_WORKSPACE, "required")
+    expect(V(L, T, 4, 16, 2, 1, FAKE, FAKE, None, ws, need - 4, None), capi.RA_ERR_WORKSPACE, "small")
+    expect(V(L, T, 4, 16, 2, 1, FAKE, FAKE, None, ws + 16, need, None), capi.RA_ERR_WORKSPACE, "256")
+    expect(V(L, T, 4, 16, 2, 1, FAKE, None, None, ws, need, None), capi.RA_ERR_NULL, "mean_loss")
 
 
 def test_permute_and_positions_errors(lib):
