@@ -112,6 +112,42 @@ def copy_calibration():
                       "launches": 3}), flush=True)
 
 
+def mfma_ceiling():
+    """The sustained bf16 matrix-core rate of this GPU and its shader clock
+    under that load, from libra_probe.so: 4 workgroups of 512 threads per CU,
+    every wavefront issuing 4 independent v_mfma_f32_32x32x16_bf16 chains.
+    The clock is the shader-clock counter over the constant-rate counter of
+    each workgroup's first wavefront (median over workgroups)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(HERE, "blockwise_online_softmax_amd", "libra_probe.so"))
+    fn = lib.ra_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = 4 * cus, 2048
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+    clk = torch.empty(2 * wgs, dtype=torch.int64, device="cuda")
+    ms, khz = ctypes.c_float(), ctypes.c_int()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for _ in range(4):  # the first launches ramp the clock
+        rc = fn(wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clk.data_ptr()),
+                ctypes.byref(ms), ctypes.byref(khz), stream)
+        if rc != 0:
+            raise RuntimeError(f"ra_probe_mfma failed with HIP error {rc}")
+        best = ms.value if best is None else min(best, ms.value)
+    c = clk.cpu().numpy().reshape(-1, 2).astype(np.float64)
+    mhz = float(np.median(c[:, 0] / c[:, 1])) * khz.value / 1e3
+    flops = wgs * 8 * iters * 4 * 32768.0
+    return {"tflops": round(flops / (best * 1e-3) / 1e12, 1), "sclk_mhz": round(mhz, 0),
+            "spec_tflops_at_that_clock": round(cus * 4 * 1024 * mhz * 1e6 / 1e12, 1),
+            "workgroups": wgs, "mfma_per_wave": iters * 4}
+
+
 def recorded_traffic(workload):
     """HBM bytes per launch of the attention kernel from the committed counter
     record (profiles/attn_mfma_<workload>_traffic.json), or None when there is
@@ -492,6 +528,8 @@ def main():
     q_tokens = qd.shape[2]
     props = torch.cuda.get_device_properties(0)
 
+    ceiling = mfma_ceiling()
+    ceiling["attention_kernel_frac_of_ceiling"] = round(kern_tflops / ceiling["tflops"], 4)
     cpu = None
     errs = None
     if not args.no_cpu_baseline:
@@ -526,6 +564,7 @@ def main():
             "traffic": recorded_traffic(args.workload),
             "kernel_ms": round(kern_ms, 4),
         },
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "sampled_max_err": None if errs is None else {"out": errs[0], "lse": errs[1]},
         "device": {"name": props.name, "cus": props.multi_processor_count,

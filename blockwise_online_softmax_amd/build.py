@@ -1,7 +1,8 @@
-"""Build libra.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Build libra.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+libra_probe.so (bench.py's MFMA-ceiling and clock probe, not part of the ABI).
 
 Usage: python -m blockwise_online_softmax_amd.build   (or __graft_entry__.build())
-The library is written next to this file; nothing is installed.
+The libraries are written next to this file; nothing is installed.
 """
 
 import os
@@ -13,6 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libra.so")
+PROBE_LIB = os.path.join(HERE, "libra_probe.so")
+PROBE_SOURCE = "ra_probe.hip"
 
 SOURCES = ["ra_api.cpp", "ra_aux.hip", "ra_attn_valu.hip", "ra_attn_mfma.hip", "ra_merge.hip",
            "ra_vocab_ce.hip"]
@@ -36,12 +39,13 @@ def hipcc():
 
 
 def build(verbose=False, jobs=4):
-    """Compile every source to an object in parallel, then link libra.so."""
+    """Compile every source to an object in parallel, then link libra.so and
+    libra_probe.so."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in SOURCES + [PROBE_SOURCE]:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
@@ -66,12 +70,13 @@ def build(verbose=False, jobs=4):
             print("\n".join(lines))
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + lib_objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 
