@@ -327,6 +327,13 @@ ra_status ra_vocab_ce_shard(const void* logits, int64_t ld, const int64_t* targe
     return fail(RA_ERR_NULL, "m, z_sum and pred must be non-NULL");
   if (!aligned(m, 4) || !aligned(z_sum, 4) || !aligned(pred, 4))
     return fail(RA_ERR_SHAPE, "m / z_sum / pred misaligned");
+  {
+    const int64_t es = dtype == RA_BF16 ? 2 : 4;
+    const span ins[2] = {{logits, ((N - 1) * ld + V_loc) * es, -1}, {target, N * 8, -2}};
+    const span outs[3] = {{m, N * 4, 1}, {z_sum, N * 4, 2}, {pred, N * 4, 3}};
+    if (!aliasing_ok(outs, 3, ins, 2))
+      return fail(RA_ERR_SHAPE, "m / z_sum / pred overlap each other or an input");
+  }
   (void)hipGetLastError();
   s = hip_status(ra::launch_ce_stats(logits, ld, target, N, V_loc, vocab_start, 1, dtype, m, z_sum,
                                      pred, (hipStream_t)stream),
@@ -343,6 +350,13 @@ ra_status ra_vocab_ce_combine(const float* m, const float* z_sum, const float* p
   if (!aligned(m, 4) || !aligned(z_sum, 4) || !aligned(pred, 4) || !aligned(loss, 4) ||
       (lse != nullptr && !aligned(lse, 4)))
     return fail(RA_ERR_SHAPE, "buffers misaligned");
+  {
+    const int64_t sb = (int64_t)t * N * 4;
+    const span ins[3] = {{m, sb, -1}, {z_sum, sb, -2}, {pred, sb, -3}};
+    const span outs[2] = {{loss, N * 4, 1}, {lse, lse != nullptr ? N * 4 : 0, 2}};
+    if (!aliasing_ok(outs, 2, ins, 3))
+      return fail(RA_ERR_SHAPE, "loss / lse overlap each other or an input");
+  }
   (void)hipGetLastError();
   ra_status s = hip_status(ra::launch_ce_combine(m, z_sum, pred, t, N, loss, lse, nullptr, nullptr,
                                                  (hipStream_t)stream),
@@ -366,6 +380,11 @@ ra_status ra_vocab_ce_grad(const void* logits, int64_t ld, const int64_t* target
   const uintptr_t g0 = (uintptr_t)grad, g1 = g0 + (uintptr_t)(((N - 1) * ldg + V_loc) * es);
   const uintptr_t l0 = (uintptr_t)logits, l1 = l0 + (uintptr_t)(((N - 1) * ld + V_loc) * es);
   if (g0 < l1 && l0 < g1) return fail(RA_ERR_SHAPE, "grad overlaps the logits");
+  {
+    const span ins[2] = {{target, N * 8, -1}, {lse, N * 4, -2}};
+    const span outs[1] = {{grad, (int64_t)(g1 - g0), 1}};
+    if (!aliasing_ok(outs, 1, ins, 2)) return fail(RA_ERR_SHAPE, "grad overlaps target or lse");
+  }
   (void)hipGetLastError();
   s = hip_status(ra::launch_ce_grad(logits, ld, target, lse, N, V_loc, vocab_start, 1, scale,
                                     dtype, grad, ldg, (hipStream_t)stream),
@@ -398,6 +417,13 @@ ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int6
   if ((int64_t)ws_bytes < w.total)
     return fail(RA_ERR_WORKSPACE, "workspace too small: %zu < %lld", ws_bytes, (long long)w.total);
   if (!aligned(ws, 256)) return fail(RA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  {
+    const int64_t es = dtype == RA_BF16 ? 2 : 4;
+    const span ins[3] = {{logits, N * V * es, -1}, {target, N * 8, -2}, {ws, w.total, -3}};
+    const span outs[3] = {{loss, N * 4, 1}, {mean_loss, 4, 2}, {lse, lse != nullptr ? N * 4 : 0, 3}};
+    if (!aliasing_ok(outs, 3, ins, 3))
+      return fail(RA_ERR_SHAPE, "loss / mean_loss / lse overlap each other, an input or the workspace");
+  }
   char* base = static_cast<char*>(ws);
   float* st = reinterpret_cast<float*>(base + w.stats);
   float* partial = reinterpret_cast<float*>(base + w.partial);

@@ -194,14 +194,15 @@ ra_status ra_merge(const void* out_a, const float* lse_a, const void* out_b, con
  *   pred[r]  = z[r][target[r] - vocab_start] if the shard owns target[r]
  *              (vocab_start <= target[r] < vocab_start + V_loc), else 0.
  * A row of -inf logits gives m = -inf, z_sum = 0.  m, z_sum, pred: [N] fp32;
- * target: [N].  N < 2^31. */
+ * target: [N].  N < 2^31.  No output may overlap another or an input. */
 ra_status ra_vocab_ce_shard(const void* logits, int64_t ld, const int64_t* target, int64_t N,
                             int64_t V_loc, int64_t vocab_start, ra_dtype dtype, float* m,
                             float* z_sum, float* pred, void* stream);
 
 /* Combine the statistics of t shards ([t, N] each, shard k's rows at k*N):
  * M = max_k m_k, Z = sum_k z_sum_k exp(m_k - M), P = sum_k pred_k;
- * loss[r] = M + log Z - P and, unless lse is NULL, lse[r] = M + log Z. */
+ * loss[r] = M + log Z - P and, unless lse is NULL, lse[r] = M + log Z.
+ * loss and lse may not overlap each other or the inputs. */
 ra_status ra_vocab_ce_combine(const float* m, const float* z_sum, const float* pred, int t,
                               int64_t N, float* loss, float* lse, void* stream);
 
@@ -209,7 +210,8 @@ ra_status ra_vocab_ce_combine(const float* m, const float* z_sum, const float* p
  * logits: grad[r][j] = scale * (exp(z[r][j] - lse[r]) - [j == target[r] -
  * vocab_start]), written in `dtype` (bf16 rounded to nearest even) with row
  * stride ldg.  lse from ra_vocab_ce_combine / ra_vocab_ce; scale = 1/N gives
- * the gradient of the mean loss.  grad must not overlap the logits.
+ * the gradient of the mean loss.  grad must not overlap the logits, target
+ * or lse.
  * N x ceil(V_loc x element size / 4096) < 2^31. */
 ra_status ra_vocab_ce_grad(const void* logits, int64_t ld, const int64_t* target, const float* lse,
                            int64_t N, int64_t V_loc, int64_t vocab_start, float scale,
@@ -223,7 +225,8 @@ size_t ra_vocab_ce_workspace_bytes(int64_t N, int t);
  * reduced by the shard kernel, then combined.  loss: [N] fp32; mean_loss: one
  * fp32 (device), the mean of loss summed in a fixed order (deterministic);
  * lse: [N] fp32 or NULL.  ws: at least ra_vocab_ce_workspace_bytes(N, t)
- * bytes, 256-byte aligned. */
+ * bytes, 256-byte aligned.  The outputs may not overlap each other, the
+ * inputs or the workspace. */
 ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int64_t V, int t,
                       ra_dtype dtype, float* loss, float* mean_loss, float* lse, void* ws,
                       size_t ws_bytes, void* stream);

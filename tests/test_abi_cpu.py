@@ -177,7 +177,11 @@ def test_vocab_ce_errors(lib):
     expect(S(L + 1, 16, T, 4, 16, 0, 1, *outs, None), capi.RA_ERR_SHAPE, "misaligned")
     expect(S(L, 16, T + 4, 4, 16, 0, 1, *outs, None), capi.RA_ERR_SHAPE, "misaligned")
     expect(S(L, 16, T, 4, 16, 0, 1, None, outs[1], outs[2], None), capi.RA_ERR_NULL, "z_sum")
+    expect(S(L, 16, T, 4, 16, 0, 1, outs[0], outs[0] + 8, outs[2], None), capi.RA_ERR_SHAPE, "overlap")
+    expect(S(L, 16, T, 4, 16, 0, 1, L + 64, outs[1], outs[2], None), capi.RA_ERR_SHAPE, "overlap")
     C = lib.ra_vocab_ce_combine
+    expect(C(*outs, 2, 4, outs[1] + 4, None, None), capi.RA_ERR_SHAPE, "overlap")
+    expect(C(*outs, 2, 4, FAKE, FAKE + 8, None), capi.RA_ERR_SHAPE, "overlap")
     expect(C(*outs, 0, 4, FAKE, None, None), capi.RA_ERR_SHAPE, "t must")
     expect(C(*outs, 2, 4, None, None, None), capi.RA_ERR_NULL, "loss")
     G = lib.ra_vocab_ce_grad
@@ -198,6 +202,9 @@ def test_vocab_ce_errors(lib):
     expect(V(L, T, 4, 16, 2, 1, FAKE, FAKE, None, ws, need - 4, None), capi.RA_ERR_WORKSPACE, "small")
     expect(V(L, T, 4, 16, 2, 1, FAKE, FAKE, None, ws + 16, need, None), capi.RA_ERR_WORKSPACE, "256")
     expect(V(L, T, 4, 16, 2, 1, FAKE, None, None, ws, need, None), capi.RA_ERR_NULL, "mean_loss")
+    expect(V(L, T, 4, 16, 2, 1, FAKE, ws + 64, None, ws, need, None), capi.RA_ERR_SHAPE, "overlap")
+    expect(V(L, T, 4, 16, 2, 1, L, FAKE + (9 << 20), None, ws, need, None), capi.RA_ERR_SHAPE, "overlap")
+    expect(G(L, 16, T, lse, 4, 16, 0, 1.0, 1, lse - 16, 16, None), capi.RA_ERR_SHAPE, "overlap")
 
 
 def test_permute_and_positions_errors(lib):
