@@ -187,3 +187,35 @@ def test_vocab_ce_full_size():
     bad = np.abs(got - ref) > np.abs(ref) * 2.0 ** -8 + tol_p
     log(f"  sampled grad: over bound {int(bad.sum())}")
     assert not bad.any()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_vocab_ce_special_values(dtype):
+    """Rows with -inf logits (a whole shard of them, or all but the target),
+    a NaN logit and a +inf logit, against the oracle: an empty shard adds
+    nothing, a NaN or +inf logit makes the row's loss NaN."""
+    N, V, t = 6, 64, 4
+    log(f"vocab ce special values {dtype}")
+    z, tg = make(N, V, dtype, 641)
+    z = z.float()
+    tg[0] = 37
+    z[0] = -float("inf")
+    z[0, 37] = 1.5                  # only the target is finite: loss 0, lse 1.5
+    z[1, 0:16] = -float("inf")      # shard 0 empty
+    z[2, 55] = float("nan")         # NaN in shard 3
+    z[3, 20] = float("inf")         # +inf in shard 1
+    z = z.to(dtype)
+    rl, _, rlse = O4.vocab_parallel(z, tg.numpy(), t)
+    loss = torch.empty(N, dtype=torch.float32, device="cuda")
+    lse = torch.empty(N, dtype=torch.float32, device="cuda")
+    mean = torch.empty(1, dtype=torch.float32, device="cuda")
+    ra.ra_vocab_ce(z.cuda(), tg.cuda(), t, loss, mean, lse)
+    torch.cuda.synchronize()
+    gl, gs = to_np(loss), to_np(lse)
+    assert np.array_equal(np.isnan(gl), np.isnan(rl)), (gl, rl)
+    assert np.isnan(gl[2]) and np.isnan(gl[3])
+    assert gl[0] == 0.0 and gs[0] == 1.5
+    fin = np.isfinite(rl)
+    m = np.nan_to_num(z.float().numpy(), nan=0.0, posinf=0.0, neginf=0.0).max(axis=1)
+    check_rows(gl[fin], rl[fin], loss_tol(m[fin], V // t, rl[fin]), "finite rows")
+    assert np.isnan(float(mean.item()))  # the mean of rows that include NaN
