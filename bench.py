@@ -115,9 +115,11 @@ def copy_calibration():
 def mfma_ceiling():
     """The sustained bf16 matrix-core rate of this GPU and its shader clock
     under that load, from libra_probe.so: 4 workgroups of 512 threads per CU,
-    every wavefront issuing 4 independent v_mfma_f32_32x32x16_bf16 chains.
-    The clock is the shader-clock counter over the constant-rate counter of
-    each workgroup's first wavefront (median over workgroups)."""
+    every wavefront issuing 4 independent v_mfma_f32_32x32x16_bf16 chains, on
+    operands that look like N(0,1) bf16 data (the clock under MFMA load
+    depends on how many operand bits toggle) and, for reference, on small
+    constants.  The clock is the shader-clock counter over the constant-rate
+    counter of each workgroup's first wavefront (median over workgroups)."""
     import ctypes
 
     import torch
@@ -125,27 +127,32 @@ def mfma_ceiling():
     lib = ctypes.CDLL(os.path.join(HERE, "blockwise_online_softmax_amd", "libra_probe.so"))
     fn = lib.ra_probe_mfma
     fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    wgs, iters = 4 * cus, 2048
+    wgs, iters = 4 * cus, 16384  # ~7 ms per launch: long enough for the clock to settle
     sink = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
     clk = torch.empty(2 * wgs, dtype=torch.int64, device="cuda")
     ms, khz = ctypes.c_float(), ctypes.c_int()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    best = None
-    for _ in range(4):  # the first launches ramp the clock
-        rc = fn(wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clk.data_ptr()),
-                ctypes.byref(ms), ctypes.byref(khz), stream)
-        if rc != 0:
-            raise RuntimeError(f"ra_probe_mfma failed with HIP error {rc}")
-        best = ms.value if best is None else min(best, ms.value)
-    c = clk.cpu().numpy().reshape(-1, 2).astype(np.float64)
-    mhz = float(np.median(c[:, 0] / c[:, 1])) * khz.value / 1e3
     flops = wgs * 8 * iters * 4 * 32768.0
-    return {"tflops": round(flops / (best * 1e-3) / 1e12, 1), "sclk_mhz": round(mhz, 0),
-            "spec_tflops_at_that_clock": round(cus * 4 * 1024 * mhz * 1e6 / 1e12, 1),
-            "workgroups": wgs, "mfma_per_wave": iters * 4}
+    res = {}
+    for random, key in ((1, "random_operands"), (0, "constant_operands")):
+        best = None
+        for _ in range(3):
+            rc = fn(wgs, iters, random, ctypes.c_void_p(sink.data_ptr()),
+                    ctypes.c_void_p(clk.data_ptr()), ctypes.byref(ms), ctypes.byref(khz), stream)
+            if rc != 0:
+                raise RuntimeError(f"ra_probe_mfma failed with HIP error {rc}")
+            best = ms.value if best is None else min(best, ms.value)
+        c = clk.cpu().numpy().reshape(-1, 2).astype(np.float64)
+        mhz = float(np.median(c[:, 0] / c[:, 1])) * khz.value / 1e3
+        res[key] = {"tflops": round(flops / (best * 1e-3) / 1e12, 1), "sclk_mhz": round(mhz, 0)}
+    out = dict(res["random_operands"])
+    out["spec_tflops_at_that_clock"] = round(cus * 4 * 1024 * out["sclk_mhz"] * 1e6 / 1e12, 1)
+    out["constant_operands"] = res["constant_operands"]
+    out.update({"workgroups": wgs, "mfma_per_wave": iters * 4})
+    return out
 
 
 def recorded_traffic(workload):

@@ -6,7 +6,7 @@
 //
 // Every wavefront issues `iters` rounds of four independent
 // v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 x 2 = 32768 FLOP each) on register
-// operands; 512-thread workgroups (two wavefronts per SIMD, as the 8-wave
+// operands (random-looking bf16 or small constants); 512-thread workgroups (two wavefronts per SIMD, as the 8-wave
 // attention kernel runs).  The first wavefront of each workgroup records
 // the shader-clock counter (s_memtime) and the constant-rate counter
 // (s_memrealtime) around its loop, so clock = d(memtime) / d(realtime) x
@@ -20,13 +20,32 @@ namespace {
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
+// A roughly normal value (sum of four uniforms, centred) from a hash of the
+// element index: the MFMA's power, and with it the clock, depends on how many
+// operand bits toggle, so the operands look like N(0,1) data, not constants.
+__device__ inline float hash_normal(unsigned x) {
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    acc += (float)(x & 0xffffu) * (1.0f / 65536.0f);
+  }
+  return (acc - 2.0f) * 1.7320508f;
+}
+
+template <bool RANDOM>
 __global__ __launch_bounds__(512) void mfma_ceiling_kernel(int iters, float* sink,
                                                            unsigned long long* clk) {
   bf16x8 a, b;
+  const unsigned gid = blockIdx.x * blockDim.x + threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(float)((threadIdx.x + i) & 3);
-    b[i] = (__bf16)(float)((threadIdx.x * 3 + i) & 1);
+    a[i] = RANDOM ? (__bf16)hash_normal(gid * 16 + i) : (__bf16)(float)((threadIdx.x + i) & 3);
+    b[i] = RANDOM ? (__bf16)hash_normal(gid * 16 + 8 + i) : (__bf16)(float)((threadIdx.x * 3 + i) & 1);
   }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
   unsigned long long t0 = 0, r0 = 0;
@@ -49,7 +68,7 @@ __global__ __launch_bounds__(512) void mfma_ceiling_kernel(int iters, float* sin
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
-  if (s == -1.f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;  // keeps the MFMAs live
+  if (s == 12345.678f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;  // keeps the MFMAs live
 }
 
 }  // namespace
@@ -57,10 +76,11 @@ __global__ __launch_bounds__(512) void mfma_ceiling_kernel(int iters, float* sin
 extern "C" {
 
 // Runs `wgs` workgroups x `iters` rounds on `stream`, returns 0 or a HIP error
-// code.  sink: >= wgs * 512 floats, clk: 2 * wgs uint64 (device buffers,
+// code.  random != 0: operands drawn like N(0,1) data; 0: small constants.
+// sink: >= wgs * 512 floats, clk: 2 * wgs uint64 (device buffers,
 // caller-owned); *ms: the launch's elapsed time (HIP events); *wall_khz: the
 // rate of the s_memrealtime counter.
-int ra_probe_mfma(int wgs, int iters, float* sink, unsigned long long* clk, float* ms,
+int ra_probe_mfma(int wgs, int iters, int random, float* sink, unsigned long long* clk, float* ms,
                   int* wall_khz, void* stream) {
   if (wgs < 1 || iters < 1 || sink == nullptr || clk == nullptr || ms == nullptr ||
       wall_khz == nullptr)
@@ -77,7 +97,10 @@ int ra_probe_mfma(int wgs, int iters, float* sink, unsigned long long* clk, floa
     return (int)e;
   }
   hipEventRecord(ev0, s);
-  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(wgs), dim3(512), 0, s, iters, sink, clk);
+  if (random)
+    hipLaunchKernelGGL(mfma_ceiling_kernel<true>, dim3(wgs), dim3(512), 0, s, iters, sink, clk);
+  else
+    hipLaunchKernelGGL(mfma_ceiling_kernel<false>, dim3(wgs), dim3(512), 0, s, iters, sink, clk);
   e = hipGetLastError();
   hipEventRecord(ev1, s);
   if (e == hipSuccess) e = hipEventSynchronize(ev1);
