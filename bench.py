@@ -228,13 +228,21 @@ def cpu_baseline(q, k, v, cfg, layout, device, seconds, gpu_out=None, gpu_lse=No
     }, errs
 
 
-def timed(fn, steps, warmup, stream):
-    """Mean ms of fn() over `steps` launches, HIP events on `stream`."""
+def timed(fn, steps, warmup, stream, min_warm_s=0.1):
+    """Mean ms of fn() over `steps` launches, HIP events on `stream`.  The
+    warm-up runs `warmup` calls and then keeps calling until `min_warm_s`
+    seconds have passed: the shader clock ramps over the first tens of
+    milliseconds of load, longer than a few calls of a sub-millisecond
+    kernel take."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        fn()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for a, b in ev:
