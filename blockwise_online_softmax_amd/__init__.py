@@ -11,7 +11,8 @@ memory and streams.  Build the library with
 
 from .capi import (  # noqa: F401
     RA_BF16, RA_F32, RA_MASK_CAUSAL, RA_MASK_NONE, RA_CONTIGUOUS, RA_STRIPED, RA_ZIGZAG,
-    LAYOUT_IDS, State, load, last_error, ra_block_step, ra_finalize, ra_merge, ra_permute,
+    LAYOUT_IDS, State, load, last_error, ra_block_step, ra_finalize, ra_layout_position, ra_merge,
+    ra_permute,
     ra_positions, ra_ring, ra_ring_workspace_bytes, ra_state_init, ra_state_merge, ra_version,
     ra_vocab_ce, ra_vocab_ce_combine, ra_vocab_ce_grad, ra_vocab_ce_shard,
     ra_vocab_ce_workspace_bytes,

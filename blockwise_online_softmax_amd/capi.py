@@ -35,7 +35,8 @@ RA_ZIGZAG = 2
 LAYOUT_IDS = {"contiguous": RA_CONTIGUOUS, "striped": RA_STRIPED, "zigzag": RA_ZIGZAG}
 
 EXPORTED = ["ra_state_init", "ra_block_step", "ra_finalize", "ra_ring",
-            "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_state_merge",
+            "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_layout_position",
+            "ra_state_merge",
             "ra_merge", "ra_vocab_ce_shard", "ra_vocab_ce_combine", "ra_vocab_ce_grad",
             "ra_vocab_ce_workspace_bytes", "ra_vocab_ce", "ra_last_error", "ra_version"]
 
@@ -77,6 +78,7 @@ def load(path=None):
         "ra_ring_workspace_bytes": (sz, [dims_p, i32, i32, i32]),
         "ra_permute": (i32, [vp, vp, i64, i64, i64, i32, i32, i32, vp]),
         "ra_positions": (i32, [vp, i64, i32, i32, i32, vp]),
+        "ra_layout_position": (i64, [i64, i32, i32, i32, i64]),
         "ra_state_merge": (i32, [state_p, state_p, state_p, vp]),
         "ra_merge": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "ra_vocab_ce_shard": (i32, [vp, i64, vp, i64, i64, i64, i32, vp, vp, vp, vp]),
@@ -244,6 +246,15 @@ def ra_positions(pos, S, N, layout, device=-1, stream=None):
     _require(pos, "pos", _torch().int32)
     _check(load().ra_positions(_ptr(pos), int(S), int(N), LAYOUT_IDS.get(layout, layout),
                                int(device), _stream(stream)), "ra_positions")
+
+
+def ra_layout_position(S, N, layout, device, index):
+    """Global token position of one index (host; the kernels' layout map)."""
+    v = load().ra_layout_position(int(S), int(N), LAYOUT_IDS.get(layout, layout), int(device),
+                                  int(index))
+    if v < 0:
+        raise ValueError(f"ra_layout_position: {last_error()}")
+    return int(v)
 
 
 def ra_state_merge(a, b, out, stream=None):

@@ -145,7 +145,7 @@ hipError_t launch_attention(const ra::AttnParams& p, int D, int dtype, bool caus
 
 extern "C" {
 
-int ra_version(void) { return 102; }
+int ra_version(void) { return 103; }
 
 const char* ra_last_error(void) { return g_err; }
 
@@ -555,15 +555,34 @@ ra_status ra_permute(const void* src, void* dst, int64_t outer, int64_t S, int64
   return s == RA_OK ? ok() : s;
 }
 
-ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int device,
-                       void* stream) {
-  if (pos == nullptr) return fail(RA_ERR_NULL, "pos must be non-NULL");
+static ra_status check_layout_args(int64_t S, int N, ra_layout layout, int device) {
   if (!layout_ok(layout)) return fail(RA_ERR_ENUM, "unknown layout %d", (int)layout);
   if (S < 1 || S >= kMaxSeq || N < 1) return fail(RA_ERR_SHAPE, "S, N must be >= 1, S < 2^31");
   if (device < -1 || device >= N) return fail(RA_ERR_ENUM, "device must be -1 or in [0, N)");
   if (S % N != 0) return fail(RA_ERR_SHAPE, "S not divisible by N");
   if (layout == RA_ZIGZAG && S % (2 * (int64_t)N) != 0)
     return fail(RA_ERR_SHAPE, "zigzag needs S %% 2N == 0");
+  return RA_OK;
+}
+
+int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64_t index) {
+  if (check_layout_args(S, N, layout, device) != RA_OK) return -1;
+  const int blk = (int)(S / N);
+  if (index < 0 || index >= (device < 0 ? S : blk)) {
+    fail(RA_ERR_SHAPE, "index out of range");
+    return -1;
+  }
+  const int p = device < 0 ? (int)(index / blk) : device;
+  const int a = device < 0 ? (int)(index - (int64_t)p * blk) : (int)index;
+  ok();
+  return ra::layout_pos(layout, N, blk, p, a);
+}
+
+ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int device,
+                       void* stream) {
+  if (pos == nullptr) return fail(RA_ERR_NULL, "pos must be non-NULL");
+  ra_status c = check_layout_args(S, N, layout, device);
+  if (c != RA_OK) return c;
   (void)hipGetLastError();
   ra_status s = hip_status(ra::launch_positions(pos, S, N, layout, device, (hipStream_t)stream),
                            "ra_positions launch");

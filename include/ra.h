@@ -153,6 +153,14 @@ ra_status ra_permute(const void* src, void* dst, int64_t outer, int64_t S, int64
 ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int device,
                        void* stream);
 
+/* The global token position of one index, computed on the host with the same
+ * layout map the kernels use ("Module 23", "The Causal Imbalance -- and the
+ * Striped Fix"): device == -1: index i of the device-ordered sequence
+ * (S entries); device == p: index i of p's block in its local order (S/N
+ * entries).  Returns -1 (and sets ra_last_error) on invalid arguments, the
+ * same checks as ra_positions. */
+int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64_t index);
+
 /* Merge two states of the same rows built from disjoint key sets into `out`
  * ("Module 23", "The Math: One Block at a Time": the fold does not depend on
  * the order of blocks, so two partial folds combine like one more fold

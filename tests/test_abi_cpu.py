@@ -41,7 +41,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert n in exported, f"{n} not exported"
         assert getattr(lib, n) is not None
-    assert lib.ra_version() == 102
+    assert lib.ra_version() == 103
 
 
 def dims(B=1, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, dtype=1, scale=0.0):
@@ -205,6 +205,34 @@ def test_vocab_ce_errors(lib):
     expect(V(L, T, 4, 16, 2, 1, FAKE, ws + 64, None, ws, need, None), capi.RA_ERR_SHAPE, "overlap")
     expect(V(L, T, 4, 16, 2, 1, L, FAKE + (9 << 20), None, ws, need, None), capi.RA_ERR_SHAPE, "overlap")
     expect(G(L, 16, T, lse, 4, 16, 0, 1.0, 1, lse - 16, 16, None), capi.RA_ERR_SHAPE, "overlap")
+
+
+def test_layout_position_matches_oracle(lib):
+    """The layout map the kernels use (compiled for the host through the ABI)
+    against the oracle's maps, for every layout, whole sequences and device
+    blocks, including N = 1 and odd block counts."""
+    import numpy as np
+
+    from oracle import layouts as OL
+
+    for S, N in ((48, 4), (96, 8), (30, 3), (16, 1), (1024, 8), (64, 2)):
+        for layout in ("contiguous", "striped", "zigzag"):
+            if layout == "zigzag" and S % (2 * N):
+                assert lib.ra_layout_position(S, N, capi.LAYOUT_IDS[layout], -1, 0) == -1
+                assert "zigzag" in capi.last_error()
+                continue
+            whole = np.concatenate([OL.device_positions(S, N, layout, p) for p in range(N)])
+            got = [lib.ra_layout_position(S, N, capi.LAYOUT_IDS[layout], -1, i) for i in range(S)]
+            assert np.array_equal(np.array(got), whole), (S, N, layout)
+            for p in (0, N - 1):
+                want = OL.device_positions(S, N, layout, p)
+                got = [lib.ra_layout_position(S, N, capi.LAYOUT_IDS[layout], p, i)
+                       for i in range(S // N)]
+                assert np.array_equal(np.array(got), want), (S, N, layout, p)
+    assert lib.ra_layout_position(48, 4, 0, -1, 48) == -1 and "range" in capi.last_error()
+    assert lib.ra_layout_position(48, 4, 0, 4, 0) == -1 and "device" in capi.last_error()
+    assert lib.ra_layout_position(48, 4, 9, -1, 0) == -1 and "layout" in capi.last_error()
+    assert lib.ra_layout_position(48, 5, 0, -1, 0) == -1 and "divisible" in capi.last_error()
 
 
 def test_permute_and_positions_errors(lib):
