@@ -23,7 +23,11 @@ def test_positions(S, N, layout):
     pos = torch.empty(S, dtype=torch.int32, device="cuda")
     ra.ra_positions(pos, S, N, layout, -1)
     want = OL.permuted_positions(S, N, layout)
-    assert np.array_equal(pos.cpu().numpy(), want)
+    got = pos.cpu().numpy()
+    assert np.array_equal(got, want)
+    # the host copy of the same map (ra_layout_position) agrees with the kernel
+    for i in sorted({0, 1, S // 2, S - 2, S - 1}):
+        assert ra.ra_layout_position(S, N, layout, -1, i) == got[i]
     for p in (0, N // 2, N - 1):
         pp = torch.empty(S // N, dtype=torch.int32, device="cuda")
         ra.ra_positions(pp, S, N, layout, p)

@@ -76,6 +76,7 @@ BF16_CASES = [
     (1, 4, 4, 4096, 8, 128),   # blocks of 512, many tiles
     (1, 4, 2, 1200, 4, 128),   # blocks of 300: 256-row query tiles with a ragged second tile
     (1, 2, 1, 1020, 4, 128),   # blocks of 255: the largest block on 128-row query tiles
+    (2, 8, 1, 2048, 4, 128),   # batch 2, 8 query heads per key/value head, blocks of 512
 ]
 
 
