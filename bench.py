@@ -228,12 +228,18 @@ def cpu_baseline(q, k, v, cfg, layout, device, seconds, gpu_out=None, gpu_lse=No
     }, errs
 
 
-def timed(fn, steps, warmup, stream, min_warm_s=0.1):
-    """Mean ms of fn() over `steps` launches, HIP events on `stream`.  The
-    warm-up runs `warmup` calls and then keeps calling until `min_warm_s`
-    seconds have passed: the shader clock ramps over the first tens of
-    milliseconds of load, longer than a few calls of a sub-millisecond
-    kernel take."""
+def ms_stats(ms):
+    """Mean, median and minimum of per-launch times in ms."""
+    return {"mean": round(float(np.mean(ms)), 4), "median": round(float(np.median(ms)), 4),
+            "min": round(float(np.min(ms)), 4), "n": len(ms)}
+
+
+def timed(fn, steps, warmup, stream, min_warm_s=0.1, stats=False):
+    """Mean ms of fn() over `steps` launches, HIP events on `stream` (with
+    stats=True: the mean, median and minimum).  The warm-up runs `warmup`
+    calls and then keeps calling until `min_warm_s` seconds have passed: the
+    shader clock ramps over the first tens of milliseconds of load, longer than
+    a few calls of a sub-millisecond kernel take."""
     import torch
 
     for _ in range(warmup):
@@ -250,7 +256,8 @@ def timed(fn, steps, warmup, stream, min_warm_s=0.1):
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return ms_stats(ms) if stats else float(np.mean(ms))
 
 
 def step_sweep(args):
@@ -318,10 +325,13 @@ def layout_balance(args):
     for layout in ("contiguous", "striped", "zigzag"):
         nws = ra.ra_ring_workspace_bytes(qd, kd, N, layout, -1)
         ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
-        t_whole = timed(lambda: ra.ra_ring(qd, kd, vd, out, lse, N, layout, True, -1, ws,
-                                           stream=stream), args.steps, args.warmup, stream)
+        st_whole = timed(lambda: ra.ra_ring(qd, kd, vd, out, lse, N, layout, True, -1, ws,
+                                            stream=stream), args.steps, args.warmup, stream,
+                         stats=True)
+        t_whole = st_whole["mean"]
         rec = {"metric": "causal ring layout balance (64K tokens, N=8)", "layout": layout,
-               "whole_ring_ms": round(t_whole, 3)}
+               "whole_ring_ms": round(t_whole, 3), "whole_ring_ms_median": st_whole["median"],
+               "whole_ring_ms_min": st_whole["min"]}
         # device-order copies of Q, K, V (the shares' inputs); permute / un-permute timing
         qp, kp, vp = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
         if layout != "contiguous":
@@ -579,6 +589,7 @@ def main():
             "traffic": recorded_traffic(args.workload),
             "kernel_ms": round(kern_ms, 4),
         },
+        "launch_ms": ms_stats(ev_ms),
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "sampled_max_err": None if errs is None else {"out": errs[0], "lse": errs[1]},
