@@ -91,55 +91,118 @@ __global__ __launch_bounds__(kRowsPerWG * 4) void attn_valu_kernel(AttnParams P)
     for (int e = 0; e < DL; ++e) o[e] = 0.f;
   }
 
-  for (int s = 0; s < P.nkblk; ++s) {
-    const int j = ((dev - s) % P.nkblk + P.nkblk) % P.nkblk;  // ring order
-    const int64_t kb0 = (int64_t)j * P.klen;
-    for (int a0 = 0; a0 < P.klen; a0 += kChunk) {
-      const int n = min(kChunk, P.klen - a0);
-      float sc[kChunk];
-      bool any = false;
+  // Folds the chunk's first n keys into (m, l, o); kv(kk, e, vsel) gives
+  // element e of this lane's part of key kk's row (vsel = 0) or value row
+  // (vsel = 1), kp(kk) the key's global position (used when CAUSAL).
+  auto fold = [&](int n, auto&& kv, auto&& kp) {
+    float sc[kChunk];
+    bool any = false;
+#pragma unroll
+    for (int kk = 0; kk < kChunk; ++kk) {
+      const bool valid = kk < n;
+      bool vis = valid;
+      if (CAUSAL && valid) vis = kp(kk) <= qpos;
+      float d = 0.f;
+      if (valid) {
+#pragma unroll
+        for (int e = 0; e < DL; ++e) d = fmaf(q[e], kv(kk, e, 0), d);
+      }
+      d += __shfl_xor(d, 1);
+      d += __shfl_xor(d, 2);
+      sc[kk] = vis ? d * P.scale : -__builtin_inff();
+      any |= vis;
+    }
+    if (!__any(any)) return;
+    float cmax = -__builtin_inff();
+#pragma unroll
+    for (int kk = 0; kk < kChunk; ++kk) cmax = fmaxf(cmax, sc[kk]);
+    const float mnew = fmaxf(m, cmax);
+    if (mnew > -__builtin_inff()) {
+      const float alpha = expf(m - mnew);  // m = -inf gives 0
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) o[e] *= alpha;
 #pragma unroll
       for (int kk = 0; kk < kChunk; ++kk) {
-        const bool valid = kk < n;
-        bool vis = valid;
-        if (CAUSAL && valid) {
-          const int kp = POS == POS_ARRAY ? P.k_pos[kb0 + a0 + kk]
-                                          : layout_pos(P.layout, P.N, P.blk, j, a0 + kk);
-          vis = kp <= qpos;
-        }
-        float d = 0.f;
-        if (valid) {
-          const T* kr = Kp + (kb0 + a0 + kk) * D;
+        // The value rows of every key in range are read whether or not the
+        // key is visible (a masked key gets p = 0), so their loads do not
+        // wait for the scores and share a memory round trip with the keys.
+        if (kk < n) {
+          const float p = sc[kk] > -__builtin_inff() ? expf(sc[kk] - mnew) : 0.f;
+          l += p;
 #pragma unroll
-          for (int e = 0; e < DL; ++e) d = fmaf(q[e], ld<T>(kr + e), d);
+          for (int e = 0; e < DL; ++e) o[e] = fmaf(p, kv(kk, e, 1), o[e]);
         }
-        d += __shfl_xor(d, 1);
-        d += __shfl_xor(d, 2);
-        sc[kk] = vis ? d * P.scale : -__builtin_inff();
-        any |= vis;
       }
-      if (!__any(any)) continue;
-      float cmax = -__builtin_inff();
+      m = mnew;
+    }
+  };
+  auto ring_block = [&](int s) { return ((dev - s) % P.nkblk + P.nkblk) % P.nkblk; };
+
+  if constexpr (DL <= 2) {
+    // Head dim 8: a chunk's key and value rows and key positions fit in
+    // registers.  Chunks are cut from the ring-ordered key sequence as a whole
+    // (block after block, across block boundaries), and the next chunk is read
+    // while this one is folded, so short blocks do not each wait for memory.
+    const int total = P.nkblk * P.klen;
+    float kc[kChunk][DL], vc[kChunk][DL];
+    int pc[kChunk];
+    auto load = [&](int f0, float (&kd)[kChunk][DL], float (&vd)[kChunk][DL], int (&pd)[kChunk]) {
+      // key f0 + kk is index a of ring step sb (block j); one division per
+      // chunk, then (a, j) advance key by key
+      int sb = f0 / P.klen;
+      int a = f0 - sb * P.klen;
+      int j = ring_block(sb);
 #pragma unroll
-      for (int kk = 0; kk < kChunk; ++kk) cmax = fmaxf(cmax, sc[kk]);
-      const float mnew = fmaxf(m, cmax);
-      if (mnew > -__builtin_inff()) {
-        const float alpha = expf(m - mnew);  // m = -inf gives 0
-        l *= alpha;
+      for (int kk = 0; kk < kChunk; ++kk) {
+        if (f0 + kk < total) {
+          const int64_t r = (int64_t)j * P.klen + a;
 #pragma unroll
-        for (int e = 0; e < DL; ++e) o[e] *= alpha;
-#pragma unroll
-        for (int kk = 0; kk < kChunk; ++kk) {
-          if (sc[kk] > -__builtin_inff()) {
-            const float p = expf(sc[kk] - mnew);
-            l += p;
-            const T* vr = Vp + (kb0 + a0 + kk) * D;
-#pragma unroll
-            for (int e = 0; e < DL; ++e) o[e] = fmaf(p, ld<T>(vr + e), o[e]);
+          for (int e = 0; e < DL; ++e) {
+            kd[kk][e] = ld<T>(Kp + r * D + e);
+            vd[kk][e] = ld<T>(Vp + r * D + e);
+          }
+          pd[kk] = !CAUSAL ? 0 : POS == POS_ARRAY ? P.k_pos[r] : layout_pos(P.layout, P.N, P.blk, j, a);
+          if (++a == P.klen) {  // next ring step: the block before j
+            a = 0;
+            j = j == 0 ? P.nkblk - 1 : j - 1;
           }
         }
-        m = mnew;
       }
+    };
+    load(0, kc, vc, pc);
+    for (int f0 = 0; f0 < total; f0 += kChunk) {
+      const bool more = f0 + kChunk < total;
+      float kn[kChunk][DL], vn[kChunk][DL];
+      int pn[kChunk];
+      if (more) load(f0 + kChunk, kn, vn, pn);
+      fold(min(kChunk, total - f0),
+           [&](int kk, int e, int vsel) { return vsel ? vc[kk][e] : kc[kk][e]; },
+           [&](int kk) { return pc[kk]; });
+      if (!more) break;
+#pragma unroll
+      for (int kk = 0; kk < kChunk; ++kk) {
+        pc[kk] = pn[kk];
+#pragma unroll
+        for (int e = 0; e < DL; ++e) {
+          kc[kk][e] = kn[kk][e];
+          vc[kk][e] = vn[kk][e];
+        }
+      }
+    }
+  } else {
+    for (int s = 0; s < P.nkblk; ++s) {
+      const int j = ring_block(s);
+      const int64_t kb0 = (int64_t)j * P.klen;
+      for (int a0 = 0; a0 < P.klen; a0 += kChunk)
+        fold(min(kChunk, P.klen - a0),
+             [&](int kk, int e, int vsel) {
+               return ld<T>((vsel ? Vp : Kp) + (kb0 + a0 + kk) * D + e);
+             },
+             [&](int kk) {
+               return POS == POS_ARRAY ? P.k_pos[kb0 + a0 + kk]
+                                       : layout_pos(P.layout, P.N, P.blk, j, a0 + kk);
+             });
     }
   }
 
