@@ -96,6 +96,11 @@ typedef struct ra_state {
  * "The ring": the running max starts at -inf, sum and output at zero.) */
 ra_status ra_state_init(const ra_state* st, void* stream);
 
+/* Non-finite inputs.  The kernels compute each tile of keys as a whole: a
+ * masked key inside a tile that also holds visible keys enters the P.V
+ * product with weight exactly 0, so its value row must be finite (0 * inf is
+ * NaN).  Keys in tiles or blocks with no visible pair are never read. */
+
 /* Fold one key/value block into the state in place ("Module 23", "The Math:
  * One Block at a Time"): for each row, m' = max(m, max_j s_ij),
  * l = l*e^(m-m') + sum_j e^(s_ij-m'), acc = acc*e^(m-m') + sum_j e^(s_ij-m') v_j.
