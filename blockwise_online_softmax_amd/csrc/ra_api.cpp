@@ -104,9 +104,17 @@ struct WsLayout {
   int64_t q, k, v, out, lse, total;
 };
 
+// The matrix-core kernels read and write a whole striped / zigzag ring in
+// natural token order (rows addressed through the layout map); the vector
+// kernels run on device-ordered copies in the workspace.
+bool ring_natural(const ra_dims* d, int layout, int device) {
+  return device < 0 && layout != RA_CONTIGUOUS && d->dtype == RA_BF16 &&
+         ra::mfma_supports((int)d->D);
+}
+
 WsLayout ring_ws(const ra_dims* d, int layout, int device) {
   WsLayout w = {0, 0, 0, 0, 0, 0};
-  if (device >= 0 || layout == RA_CONTIGUOUS) return w;
+  if (device >= 0 || layout == RA_CONTIGUOUS || ring_natural(d, layout, device)) return w;
   const int64_t es = elem_size(d->dtype);
   const int64_t S = d->Sk;
   const int64_t qb = round256(d->B * d->Hq * S * d->D * es);
@@ -135,9 +143,9 @@ ra::AttnParams base_params(const ra_dims* d) {
 }
 
 hipError_t launch_attention(const ra::AttnParams& p, int D, int dtype, bool causal, int pos_mode,
-                            bool state_io, hipStream_t s) {
+                            bool state_io, hipStream_t s, bool natural = false) {
   if (dtype == RA_BF16 && ra::mfma_supports(D))
-    return ra::launch_attn_mfma(p, D, causal, pos_mode, state_io, s);
+    return ra::launch_attn_mfma(p, D, causal, pos_mode, state_io, natural, s);
   return ra::launch_attn_valu(p, D, dtype, causal, pos_mode, state_io, s);
 }
 
@@ -145,7 +153,7 @@ hipError_t launch_attention(const ra::AttnParams& p, int D, int dtype, bool caus
 
 extern "C" {
 
-int ra_version(void) { return 103; }
+int ra_version(void) { return 104; }
 
 const char* ra_last_error(void) { return g_err; }
 
@@ -518,7 +526,8 @@ ra_status ra_ring(const void* Q, const void* K, const void* V, void* out, float*
     p.lse = (float*)(wsb + w.lse);
   }
   s = hip_status(launch_attention(p, (int)d->D, d->dtype, causal != 0,
-                                  causal ? ra::POS_ANALYTIC : ra::POS_NONE, false, st),
+                                  causal ? ra::POS_ANALYTIC : ra::POS_NONE, false, st,
+                                  ring_natural(d, layout, device)),
                  "ring attention launch");
   if (s != RA_OK) return s;
   if (permuted) {

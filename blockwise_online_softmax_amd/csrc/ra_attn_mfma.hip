@@ -145,7 +145,7 @@ struct Tile {
   int kp;
 };
 
-template <bool CAUSAL, int POS>
+template <bool CAUSAL, int POS, bool NAT>
 struct TileWalker {
   int s, tt, j;
   bool bfull;
@@ -187,6 +187,20 @@ struct TileWalker {
       T.n = n;
       T.kp = 0;
       bool full = (n == BN);
+      if (NAT && !(CAUSAL && POS == POS_ANALYTIC)) {
+        // natural-order rows: position of the tile's keys (no mask needed)
+        T.p0 = layout_pos(P.layout, P.N, P.blk, j, a0);
+        T.stride = P.layout == RA_STRIPED ? P.N : 1;
+        T.split = BN;
+        T.p1 = T.p0;
+        if (P.layout == RA_ZIGZAG) {
+          const int c = P.blk >> 1;
+          if (a0 < c && a0 + n > c) {
+            T.split = c - a0;
+            T.p1 = layout_pos(P.layout, P.N, P.blk, j, c) - (c - a0);
+          }
+        }
+      }
       if (CAUSAL && POS == POS_ANALYTIC) {
         const int kf = layout_pos(P.layout, P.N, P.blk, j, a0);
         if (!bfull) {
@@ -226,7 +240,7 @@ struct TileWalker {
   }
 };
 
-template <int D, int NW, bool CAUSAL, int POS, bool STATE_IO>
+template <int D, int NW, bool CAUSAL, int POS, bool STATE_IO, bool NAT = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
   constexpr int NDB = D / 32;         // 32-row d blocks of O^T
@@ -272,7 +286,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   const int nrows = min(NW * 32, P.qlen - a0q);
   const int la = a0q + wave * 32 + r;           // this lane's local query row
   const bool rvalid = la < P.qlen;
-  const int64_t qrow = (int64_t)qi * P.qlen + la;
+  // the query row in Q / out / lse: device order, or (NAT) the row's natural
+  // token position
+  int64_t qrow;
+  if constexpr (NAT)
+    qrow = rvalid ? layout_pos(P.layout, P.N, P.blk, dev, la) : 0;
+  else
+    qrow = (int64_t)qi * P.qlen + la;
   const int64_t bh = (int64_t)b * P.Hq + h;
   const uint16_t* Qg = reinterpret_cast<const uint16_t*>(P.Q);
   const uint16_t* Kg =
@@ -375,8 +395,57 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     dk0 = row * ROWB + ((ph ^ (row & KMASK)) << 4);
     dv0 = row * ROWB + ((ph ^ vswz(row)) << 4);
   }
+  // natural-order rows (NAT): token stride between a tile's rows (N striped,
+  // else 1), this lane's source offsets within a copy, and the byte step
+  // between a wave's copies
+  [[maybe_unused]] unsigned dkn = 0, dvn = 0;
+  [[maybe_unused]] int64_t cstep = 0;
+  if constexpr (NAT) {
+    const int nstride = P.layout == RA_STRIPED ? P.N : 1;
+    const int row = wave * RPC + lane / UNITS;
+    const int ph = lane % UNITS;
+    dkn = (unsigned)(row * nstride * ROWB) + ((ph ^ (row & KMASK)) << 4);
+    dvn = (unsigned)(row * nstride * ROWB) + ((ph ^ vswz(row)) << 4);
+    cstep = (int64_t)NW * RPC * nstride * ROWB;
+  }
   auto issue_tile = [&](const Tile& T, lds_t* kdst) {
     lds_t* vdst = kdst + TILE_BYTES;
+    if constexpr (NAT) {
+      // Key rows in natural order: tile row kt is token (kt < split ? p0 : p1)
+      // + kt * stride.  The LDS placement (and its swizzle) is the same as
+      // for device-ordered rows; only the source rows differ.
+      const char* kn = reinterpret_cast<const char*>(Kg);
+      const char* vn = reinterpret_cast<const char*>(Vg);
+      if (T.n == BN && T.split >= BN) {
+        const char* kb = kn + (int64_t)T.p0 * ROWB;
+        const char* vb = vn + (int64_t)T.p0 * ROWB;
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) {
+          const int x = wave + NW * i;
+          unsigned ko = dkn, vo = dvn;
+          asm volatile("" : "+v"(ko), "+v"(vo));
+          dma16(kb + i * cstep + ko, kdst + x * 1024);
+          dma16(vb + i * cstep + vo, vdst + x * 1024);
+        }
+      } else {
+        const int p0 = T.p0, p1 = T.p1, split = T.split, stride = T.stride, last = T.n - 1;
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) {
+          const int x = wave + NW * i;
+          const int row = x * RPC + lane / UNITS;
+          const int ph = lane % UNITS;
+          const int rr = min(row, last);
+          const int first = rr < split ? p0 : p1;  // per-lane choice between two uniform values
+          const int64_t tok = (int64_t)first + (int64_t)rr * stride;
+          unsigned ko = (unsigned)(tok * ROWB) + ((ph ^ (row & KMASK)) << 4);
+          unsigned vo = (unsigned)(tok * ROWB) + ((ph ^ vswz(row)) << 4);
+          asm volatile("" : "+v"(ko), "+v"(vo));
+          dma16(kn + ko, kdst + x * 1024);
+          dma16(vn + vo, vdst + x * 1024);
+        }
+      }
+      return;
+    }
     const char* kb = reinterpret_cast<const char*>(Kg + T.start * D);
     const char* vb = reinterpret_cast<const char*>(Vg + T.start * D);
     if (T.n == BN) {
@@ -409,7 +478,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     }
   };
 
-  TileWalker<CAUSAL, POS> walker;
+  TileWalker<CAUSAL, POS, NAT> walker;
   walker.init(P);
   Tile cur;
   bool have = walker.next(P, dev, qmin, qmax, cur);
@@ -712,12 +781,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
 }
 
 template <int D, int NW>
-hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_io,
+hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_io, bool natural,
                     hipStream_t s) {
   AttnParams p = p0;
   p.ntq = (p.qlen + NW * 32 - 1) / (NW * 32);
   const int64_t nwg = (int64_t)p.B * p.Hq * p.nqblk * p.ntq;
   const dim3 grid((unsigned)nwg), block(NW * 64);
+  if (natural) {  // whole ring read and written in natural token order
+    if (state_io || pos_mode == POS_ARRAY) return hipErrorInvalidValue;
+    if (causal)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, true>), grid, block,
+                         0, s, p);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, false, true>), grid, block, 0,
+                         s, p);
+    return hipGetLastError();
+  }
   if (!causal) {
     if (state_io)
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, true>), grid, block, 0, s, p);
@@ -744,13 +823,13 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
 bool mfma_supports(int D) { return D == 32 || D == 64 || D == 128; }
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mode, bool state_io,
-                            hipStream_t s) {
+                            bool natural, hipStream_t s) {
   switch (D) {
-    case 32: return launch_d<32, 4>(p, causal, pos_mode, state_io, s);
-    case 64: return launch_d<64, 4>(p, causal, pos_mode, state_io, s);
+    case 32: return launch_d<32, 4>(p, causal, pos_mode, state_io, natural, s);
+    case 64: return launch_d<64, 4>(p, causal, pos_mode, state_io, natural, s);
     case 128:  // 8 waves (256 query rows) once a block has that many rows
-      return p.qlen >= 256 ? launch_d<128, 8>(p, causal, pos_mode, state_io, s)
-                           : launch_d<128, 4>(p, causal, pos_mode, state_io, s);
+      return p.qlen >= 256 ? launch_d<128, 8>(p, causal, pos_mode, state_io, natural, s)
+                           : launch_d<128, 4>(p, causal, pos_mode, state_io, natural, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -56,8 +56,10 @@ struct AttnParams {
 };
 
 // Launchers (return hipGetLastError() after the launch).
+// natural: a whole ring whose Q, K, V, out, lse are in natural token order
+// (striped / zigzag rows addressed through the layout map, no permutes).
 hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mode, bool state_io,
-                            hipStream_t s);
+                            bool natural, hipStream_t s);
 bool mfma_supports(int D);
 hipError_t launch_attn_valu(const AttnParams& p, int D, int dtype, bool causal, int pos_mode,
                             bool state_io, hipStream_t s);

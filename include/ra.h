@@ -127,14 +127,17 @@ ra_status ra_finalize(const ra_state* st, void* out, float* lse, ra_dtype out_dt
  * holds block (p - s) mod N -- then divides by l.  Blocks (and tiles) with no
  * visible pair are skipped.  Outputs: out (Q's dtype) and lse (fp32).
  *   device == -1: the whole ring on this GPU.  Q, K, V, out, lse are in
- *     natural token order; d->Sq == d->Sk == S.  Striped and zigzag layouts
- *     are permuted into device order in the workspace and back afterwards.
+ *     natural token order; d->Sq == d->Sk == S.  Under striped and zigzag
+ *     layouts, bf16 inputs with head dim 32, 64 or 128 are read and written in
+ *     place through the layout map; other inputs (fp32, head dim 8 or 16) are
+ *     permuted into device order in the workspace and back afterwards.
  *   device == p (0 <= p < N): device p's share.  Q is p's block in its local
  *     order (d->Sq == S/N), K and V are the whole sequence in device order
  *     (d->Sk == S), and out / lse come back in p's local order.
  *   causal: 0 or 1.  S % N == 0 (S % 2N == 0 for zigzag).
  *   ws / ws_bytes: workspace of at least ra_ring_workspace_bytes(...) bytes
- *   (0 for contiguous layouts and for device >= 0; ws may then be NULL). */
+ *   (0 for contiguous layouts, for device >= 0 and for bf16 with head dim 32,
+ *   64 or 128; ws may then be NULL). */
 ra_status ra_ring(const void* Q, const void* K, const void* V, void* out, float* lse,
                   const ra_dims* d, int N, ra_layout layout, int causal, int device,
                   void* ws, size_t ws_bytes, void* stream);

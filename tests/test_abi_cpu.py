@@ -41,7 +41,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert n in exported, f"{n} not exported"
         assert getattr(lib, n) is not None
-    assert lib.ra_version() == 103
+    assert lib.ra_version() == 104
 
 
 def dims(B=1, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, dtype=1, scale=0.0):
@@ -110,11 +110,13 @@ def test_ring_errors(lib):
     expect(ring(lib, dims(Sq=128), N=8, device=3), capi.RA_ERR_SHAPE, "S/N")
     expect(ring(lib, dims(), causal=2), capi.RA_ERR_ENUM, "causal")
     expect(ring(lib, dims(), out=None), capi.RA_ERR_NULL, "non-NULL")
-    need = lib.ra_ring_workspace_bytes(ctypes.byref(dims()), 8, 1, -1)
+    # fp32 inputs run on device-ordered copies in the workspace
+    f32 = dims(dtype=0)
+    need = lib.ra_ring_workspace_bytes(ctypes.byref(f32), 8, 1, -1)
     assert 0 < need < (1 << 40)
-    expect(ring(lib, dims(), layout=1), capi.RA_ERR_WORKSPACE, "required")
-    expect(ring(lib, dims(), layout=1, ws=FAKE, wsb=need - 1), capi.RA_ERR_WORKSPACE, "small")
-    expect(ring(lib, dims(), layout=2, ws=FAKE + 16, wsb=need), capi.RA_ERR_WORKSPACE, "256")
+    expect(ring(lib, f32, layout=1), capi.RA_ERR_WORKSPACE, "required")
+    expect(ring(lib, f32, layout=1, ws=FAKE, wsb=need - 1), capi.RA_ERR_WORKSPACE, "small")
+    expect(ring(lib, f32, layout=2, ws=FAKE + 16, wsb=need), capi.RA_ERR_WORKSPACE, "256")
 
 
 def test_workspace_bytes(lib):
@@ -125,11 +127,19 @@ def test_workspace_bytes(lib):
     assert ws(dims(Hq=3), 8, 0, -1) == bad and "multiple" in capi.last_error()
     assert ws(dims(), 8, 0, -1) == 0 and capi.last_error() == ""
     assert ws(dims(Sq=16), 8, 2, 0) == 0  # a device share needs no workspace
-    # 65536 tokens, 32/8 heads, D 128, bf16, striped: Q + out copies, K + V copies, lse copy
+    # bf16 with a matrix-core head dim: striped and zigzag whole rings are read
+    # and written in natural order, no workspace
     d = dims(Hq=32, Hkv=8, Sq=65536, Sk=65536)
-    q = 32 * 65536 * 128 * 2
-    kv = 8 * 65536 * 128 * 2
-    assert ws(d, 8, 1, -1) == 2 * q + 2 * kv + 32 * 65536 * 4
+    for D in (32, 64, 128):
+        assert ws(dims(Hq=32, Hkv=8, Sq=65536, Sk=65536, D=D), 8, 1, -1) == 0
+        assert ws(dims(Hq=32, Hkv=8, Sq=65536, Sk=65536, D=D), 8, 2, -1) == 0
+    # the vector kernels (fp32, or bf16 with D 8 / 16) work on device-ordered
+    # copies: Q + out copies, K + V copies, lse copy
+    for dtype, D, es in ((0, 128, 4), (1, 16, 2), (1, 8, 2)):
+        d = dims(Hq=32, Hkv=8, Sq=65536, Sk=65536, D=D, dtype=dtype)
+        q = 32 * 65536 * D * es
+        kv = 8 * 65536 * D * es
+        assert ws(d, 8, 1, -1) == 2 * q + 2 * kv + 32 * 65536 * 4
 
 
 def test_merge_errors(lib):
