@@ -546,9 +546,15 @@ def main():
     def step():
         ra.ra_ring(qd, kd, vd, out, lse, N, layout, causal, device, ws, stream=stream)
 
-    for _ in range(args.warmup):
+    # warm-up: `warmup` calls, then more until 0.5 s have passed (the shader
+    # clock ramps under load, and the XCD speed estimate averages 8 launches);
+    # synchronised, so each launch's XCD stamps land before the next call
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < 0.5:
         step()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n_warm += 1
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -568,6 +574,11 @@ def main():
     q_tokens = qd.shape[2]
     props = torch.cuda.get_device_properties(0)
 
+    speeds, nmeas = ra.ra_xcd_speeds()
+    grid, M, keep, dbeg, dcnt = ra.ra_xcd_plan(qd, kd, N, layout, causal, device, speeds)
+    xcd = {"speeds": [round(x, 4) for x in speeds], "measurements": nmeas,
+           "workgroups": grid, "items_per_xcd": M, "items_moved": int(sum(dcnt)),
+           "balance": os.environ.get("RA_XCD_BALANCE", "1") != "0"}
     ceiling = mfma_ceiling()
     ceiling["attention_kernel_frac_of_ceiling"] = round(kern_tflops / ceiling["tflops"], 4)
     cpu = None
@@ -583,6 +594,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls": n_warm,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -605,6 +617,7 @@ def main():
             "kernel_ms": round(kern_ms, 4),
         },
         "launch_ms": ms_stats(ev_ms),
+        "xcd_split": xcd,
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "sampled_max_err": None if errs is None else {"out": errs[0], "lse": errs[1]},

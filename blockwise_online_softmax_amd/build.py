@@ -18,7 +18,7 @@ PROBE_LIB = os.path.join(HERE, "libra_probe.so")
 PROBE_SOURCE = "ra_probe.hip"
 
 SOURCES = ["ra_api.cpp", "ra_aux.hip", "ra_attn_valu.hip", "ra_attn_mfma.hip", "ra_merge.hip",
-           "ra_vocab_ce.hip"]
+           "ra_vocab_ce.hip", "ra_xcd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

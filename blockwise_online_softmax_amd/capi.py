@@ -38,7 +38,8 @@ EXPORTED = ["ra_state_init", "ra_block_step", "ra_finalize", "ra_ring",
             "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_layout_position",
             "ra_state_merge",
             "ra_merge", "ra_vocab_ce_shard", "ra_vocab_ce_combine", "ra_vocab_ce_grad",
-            "ra_vocab_ce_workspace_bytes", "ra_vocab_ce", "ra_last_error", "ra_version"]
+            "ra_vocab_ce_workspace_bytes", "ra_vocab_ce", "ra_xcd_plan", "ra_xcd_speeds",
+            "ra_last_error", "ra_version"]
 
 
 class RaDims(ctypes.Structure):
@@ -87,6 +88,8 @@ def load(path=None):
                                    vp]),
         "ra_vocab_ce_workspace_bytes": (sz, [i64, i32]),
         "ra_vocab_ce": (i32, [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "ra_xcd_plan": (i64, [dims_p, i32, i32, i32, i32, vp, vp]),
+        "ra_xcd_speeds": (i32, [vp, vp, i32]),
         "ra_last_error": (ctypes.c_char_p, []),
         "ra_version": (i32, []),
     }
@@ -246,6 +249,33 @@ def ra_positions(pos, S, N, layout, device=-1, stream=None):
     _require(pos, "pos", _torch().int32)
     _check(load().ra_positions(_ptr(pos), int(S), int(N), LAYOUT_IDS.get(layout, layout),
                                int(device), _stream(stream)), "ra_positions")
+
+
+def ra_xcd_plan(q, k, N, layout, causal, device=-1, speeds=None, scale=None):
+    """Split of an ra_ring launch over the 8 XCDs for relative per-XCD speeds
+    (host only; default equal).  Returns (grid, M, keep, dbeg, dcnt); grid 0
+    means the launch is not split."""
+    d = make_dims(q, k, scale)
+    sp = (ctypes.c_float * 8)(*([1.0] * 8 if speeds is None else [float(x) for x in speeds]))
+    plan = (ctypes.c_int * 25)()
+    g = load().ra_xcd_plan(ctypes.byref(d), int(N), LAYOUT_IDS.get(layout, layout),
+                           int(bool(causal)), int(device), sp, plan)
+    if g < 0:
+        raise ValueError(f"ra_xcd_plan: {last_error()}")
+    v = list(plan)
+    return int(g), v[0], v[1:9], v[9:17], v[17:25]
+
+
+def ra_xcd_speeds(speeds=None, set=False):
+    """The current device's per-XCD speed estimate.  set=False: returns
+    (speeds, measurements).  set=True: fixes the estimate to `speeds` (no
+    more measuring), or with speeds=None returns to equal speeds and
+    measuring."""
+    sp = (ctypes.c_float * 8)(*([1.0] * 8 if speeds is None else [float(x) for x in speeds]))
+    n = ctypes.c_int(0)
+    arg = None if (set and speeds is None) else sp
+    _check(load().ra_xcd_speeds(arg, ctypes.byref(n), int(bool(set))), "ra_xcd_speeds")
+    return list(sp), int(n.value)
 
 
 def ra_layout_position(S, N, layout, device, index):

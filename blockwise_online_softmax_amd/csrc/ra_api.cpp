@@ -153,7 +153,7 @@ hipError_t launch_attention(const ra::AttnParams& p, int D, int dtype, bool caus
 
 extern "C" {
 
-int ra_version(void) { return 104; }
+int ra_version(void) { return 105; }
 
 const char* ra_last_error(void) { return g_err; }
 
@@ -456,6 +456,30 @@ size_t ra_ring_workspace_bytes(const ra_dims* d, int N, ra_layout layout, int de
   return (size_t)ring_ws(d, layout, device).total;
 }
 
+// Launch parameters of a ring over N devices (device = -1: all of them).
+static ra::AttnParams ring_params(const ra_dims* d, int N, ra_layout layout, int device) {
+  const int64_t S = d->Sk;
+  const int blk = (int)(S / N);
+  ra::AttnParams p = base_params(d);
+  p.layout = layout;
+  p.N = N;
+  p.blk = blk;
+  p.nkblk = N;
+  p.klen = blk;
+  p.Sk_tot = S;
+  p.qlen = blk;
+  if (device >= 0) {
+    p.Sq_tot = blk;
+    p.nqblk = 1;
+    p.dev0 = device;
+  } else {
+    p.Sq_tot = S;
+    p.nqblk = N;
+    p.dev0 = 0;
+  }
+  return p;
+}
+
 ra_status ra_ring(const void* Q, const void* K, const void* V, void* out, float* lse,
                   const ra_dims* d, int N, ra_layout layout, int causal, int device, void* ws,
                   size_t ws_bytes, void* stream) {
@@ -482,29 +506,12 @@ ra_status ra_ring(const void* Q, const void* K, const void* V, void* out, float*
   const int64_t es = elem_size(d->dtype);
   const int64_t row_bytes = d->D * es;
 
-  ra::AttnParams p = base_params(d);
+  ra::AttnParams p = ring_params(d, N, layout, device);
   p.Q = Q;
   p.K = K;
   p.V = V;
   p.out = out;
   p.lse = lse;
-  p.layout = layout;
-  p.N = N;
-  p.blk = blk;
-  p.nkblk = N;
-  p.klen = blk;
-  p.Sk_tot = S;
-  if (device >= 0) {
-    p.Sq_tot = blk;
-    p.nqblk = 1;
-    p.qlen = blk;
-    p.dev0 = device;
-  } else {
-    p.Sq_tot = S;
-    p.nqblk = N;
-    p.qlen = blk;
-    p.dev0 = 0;
-  }
 
   (void)hipGetLastError();
   char* wsb = (char*)ws;
@@ -572,6 +579,51 @@ static ra_status check_layout_args(int64_t S, int N, ra_layout layout, int devic
   if (layout == RA_ZIGZAG && S % (2 * (int64_t)N) != 0)
     return fail(RA_ERR_SHAPE, "zigzag needs S %% 2N == 0");
   return RA_OK;
+}
+
+int64_t ra_xcd_plan(const ra_dims* d, int N, ra_layout layout, int causal, int device,
+                    const float* speeds, int* plan) {
+  if (check_ring_args(d, N, layout, device) != RA_OK) return -1;
+  if (causal != 0 && causal != 1) {
+    fail(RA_ERR_ENUM, "causal must be 0 or 1 (got %d)", causal);
+    return -1;
+  }
+  if (speeds == nullptr || plan == nullptr) {
+    fail(RA_ERR_NULL, "speeds and plan must be non-NULL");
+    return -1;
+  }
+  for (int x = 0; x < ra::kXcds; ++x)
+    if (!(speeds[x] > 0.f) || speeds[x] > 1e6f) {
+      fail(RA_ERR_SHAPE, "speeds must be positive and finite");
+      return -1;
+    }
+  memset(plan, 0, sizeof(int) * (1 + 3 * ra::kXcds));
+  ok();
+  if (!(d->dtype == RA_BF16 && ra::mfma_supports((int)d->D))) return 0;
+  ra::AttnParams p = ring_params(d, N, layout, device);
+  int rows, per_cu;
+  ra::mfma_geometry((int)d->D, p.qlen, &rows, &per_cu);
+  p.ntq = (p.qlen + rows - 1) / rows;
+  const int64_t nwg = (int64_t)p.B * p.Hq * p.nqblk * p.ntq;
+  ra::XcdPlan X;
+  const int64_t grid = ra::xcd_plan_for(p, nwg, causal != 0, rows, per_cu, speeds, &X);
+  if (grid > 0) {
+    plan[0] = X.M;
+    for (int x = 0; x < ra::kXcds; ++x) {
+      plan[1 + x] = X.keep[x];
+      plan[1 + ra::kXcds + x] = X.dbeg[x];
+      plan[1 + 2 * ra::kXcds + x] = X.dcnt[x];
+    }
+  }
+  return grid;
+}
+
+ra_status ra_xcd_speeds(float* speeds, int* nmeas, int set) {
+  if (set != 0 && set != 1) return fail(RA_ERR_ENUM, "set must be 0 or 1 (got %d)", set);
+  const int r = ra::xcd_speeds(speeds, nmeas, set);
+  if (r == -1) return fail(RA_ERR_HIP, "no current HIP device");
+  if (r == -2) return fail(RA_ERR_SHAPE, "speeds must be positive and finite");
+  return ok();
 }
 
 int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64_t index) {

@@ -109,6 +109,21 @@ __device__ inline void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Low 40 bits of the GPU's constant-rate (100 MHz) clock; wraps after 3 hours.
+__device__ inline unsigned long long stamp40() {
+  return (unsigned long long)__builtin_amdgcn_s_memrealtime() & ((1ull << 40) - 1);
+}
+
+}  // namespace
+
+// XCD stamps of the ring launches (see XcdPlan); one copy per GPU.
+__device__ unsigned long long g_xcd_stat[2 * kXcds];
+
+namespace {
+
+// The XCD this wave runs on (hardware register XCC_ID, low 4 bits).
+__device__ inline int xcc_id() { return (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7); }
+
 __device__ inline int wave_min(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
@@ -241,7 +256,7 @@ struct TileWalker {
 };
 
 template <int D, int NW, bool CAUSAL, int POS, bool STATE_IO, bool NAT = false>
-__global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, XcdPlan X) {
   constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
   constexpr int NDB = D / 32;         // 32-row d blocks of O^T
   constexpr int UNITS = D / 8;        // 16-byte units per row
@@ -266,17 +281,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
   const int r = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item: XCD-major, then batch / kv head, longest-first tiles ----
-  const int64_t W = (int64_t)P.B * P.Hq * P.nqblk * P.ntq;
+  // ---- work item: XCD plan, then batch / kv head, longest-first tiles ----
   const int64_t w = blockIdx.x;
-  int64_t L = (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;
+  int64_t L = xcd_item(X, w);
+  if (L < 0) return;  // a slot without an item (the whole workgroup)
+  if (X.tag != 0 && w < kXcds && tid == 0) {  // the first workgroup of an XCD
+    const int x = xcc_id();
+    g_xcd_stat[x] = 0;
+    g_xcd_stat[kXcds + x] = X.tag | stamp40();
+  }
   const int G = P.Hq / P.Hkv;
   const int hg = (int)(L % G);
   L /= G;
-  const int t = P.ntq - 1 - (int)(L % P.ntq);
-  L /= P.ntq;
-  const int qi = P.nqblk - 1 - (int)(L % P.nqblk);
-  L /= P.nqblk;
+  const int nt = P.nqblk * P.ntq;
+  int qi, t;
+  item_tile(P.layout, CAUSAL && POS == POS_ANALYTIC, P.nqblk, P.ntq, NW * 32, P.blk,
+            (int)(L % nt), qi, t);
+  L /= nt;
   const int g = (int)(L % P.Hkv);
   const int b = (int)(L / P.Hkv);
   const int h = g * G + hg;
@@ -736,6 +757,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P) {
     }
   }
 
+  // (no kernel argument is live across the tile loop for this)
+  if (tid == 0) atomicMax(&g_xcd_stat[xcc_id()], stamp40());
+
   // ---- epilogue ----
   if (STATE_IO && mtrue > -__builtin_inff() && mtrue != m2) {  // move to the exact running max
     const float alpha = __builtin_amdgcn_exp2f(m2 - mtrue);
@@ -786,41 +810,66 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
   AttnParams p = p0;
   p.ntq = (p.qlen + NW * 32 - 1) / (NW * 32);
   const int64_t nwg = (int64_t)p.B * p.Hq * p.nqblk * p.ntq;
-  const dim3 grid((unsigned)nwg), block(NW * 64);
+  int rows, per_cu;
+  mfma_geometry(D, p.qlen, &rows, &per_cu);
+  const bool ring = !state_io && pos_mode != POS_ARRAY;
+  XcdPlan X;
+  const int64_t ngrid = xcd_prepare(p, nwg, causal, ring, rows, per_cu, s, &X);
+  const dim3 grid((unsigned)ngrid), block(NW * 64);
+  hipError_t e;
   if (natural) {  // whole ring read and written in natural token order
     if (state_io || pos_mode == POS_ARRAY) return hipErrorInvalidValue;
     if (causal)
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, true>), grid, block,
-                         0, s, p);
+                         0, s, p, X);
     else
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, false, true>), grid, block, 0,
-                         s, p);
-    return hipGetLastError();
+                         s, p, X);
+    e = hipGetLastError();
+    if (e == hipSuccess) xcd_after_launch(X, s);
+    return e;
   }
   if (!causal) {
     if (state_io)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, true>), grid, block, 0, s, p, X);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, false>), grid, block, 0, s, p, X);
   } else if (pos_mode == POS_ARRAY) {
     if (state_io)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, true>), grid, block, 0, s, p, X);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, false>), grid, block, 0, s, p, X);
   } else {
     if (state_io)
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, true>), grid, block, 0, s,
-                         p);
+                         p, X);
     else
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false>), grid, block, 0, s,
-                         p);
+                         p, X);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess) xcd_after_launch(X, s);
+  return e;
 }
 
 }  // namespace
 
 bool mfma_supports(int D) { return D == 32 || D == 64 || D == 128; }
+
+void* xcd_stat_address() {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_xcd_stat)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return p;
+}
+
+void mfma_geometry(int D, int qlen, int* rows, int* per_cu) {
+  const int nw = (D == 128 && qlen >= 256) ? 8 : 4;
+  *rows = nw * 32;
+  *per_cu = nw == 8 ? 1 : 2;  // one 8-wave or two 4-wave workgroups share a CU
+}
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mode, bool state_io,
                             bool natural, hipStream_t s) {

@@ -30,6 +30,73 @@ enum PosMode : int {
   POS_ARRAY = 2,     // explicit int32 arrays q_pos / k_pos, any order
 };
 
+// Work split of one launch over the GPU's 8 XCDs (the compute dies, each with
+// its own L2).  The hardware hands workgroup w to XCD w % 8 as that XCD's slot
+// w / 8.  Work items are numbered XCD-major: XCD x owns items x*M .. x*M+M-1,
+// longest first.  XCD x first runs entries dbeg[x] .. dbeg[x]+dcnt[x]-1 of the
+// donated list (the items the XCDs do not keep, XCD after XCD, each in its own
+// order), then the first keep[x] of its own items; later slots have no item.
+// An XCD that gives items away receives none, so every XCD's list ends with
+// its own shortest items.  keep = M and dcnt = 0 everywhere is the fixed
+// XCD-major order.  An item is computed the same way on any XCD, so a plan
+// changes timing, never results.
+constexpr int kXcds = 8;
+struct XcdPlan {
+  int M;  // items per XCD; 0: no split (item = workgroup index)
+  int keep[kXcds], dbeg[kXcds], dcnt[kXcds];
+  // Non-zero: the launch is measured; bits 40..63 tag its start stamps.  Every
+  // workgroup of the matrix-core kernel raises its XCD's end stamp; the first
+  // workgroup of each XCD of a measured launch clears that end stamp and writes
+  // the tagged start stamp.  Stamps: the library's per-GPU array of 2 * 8
+  // values (xcd_stat_address), [x] end and [8 + x] start of XCD x, in 10 ns
+  // ticks of the GPU's constant clock (low 40 bits).
+  unsigned long long tag;
+};
+
+// The item of workgroup w under plan X, or -1 for a slot without one.
+__host__ __device__ inline int64_t xcd_item(const XcdPlan& X, int64_t w) {
+  if (X.M == 0) return w;
+  const int x = (int)(w % kXcds), sl = (int)(w / kXcds);
+  if (sl < X.dcnt[x]) {  // a donated item
+    int idx = X.dbeg[x] + sl, y = 0;
+    while (y < kXcds - 1 && idx >= X.M - X.keep[y]) {
+      idx -= X.M - X.keep[y];
+      ++y;
+    }
+    return (int64_t)y * X.M + X.keep[y] + idx;
+  }
+  const int own = sl - X.dcnt[x];
+  return own < X.keep[x] ? (int64_t)x * X.M + own : -1;
+}
+
+// Query block qi and query tile t of the r-th item (r < nqblk * ntq, tiles of
+// `rows` rows, blocks of blk rows).  Under the causal mask a tile's work grows
+// with its last query position, so causal rings take tiles longest-first:
+// contiguous (block p holds p*blk ..): blocks, then tiles, descending;
+// striped (block p holds p, p+N, ..): tiles, then blocks, descending;
+// zigzag (block p holds chunk p, then chunk 2N-1-p): the tiles that reach the
+// second chunk, blocks ascending, then the first-chunk tiles, blocks
+// descending, tiles descending within a block.  Other launches: blocks, then
+// tiles, descending.
+//
+// Written without branches: a branch on the layout here changes how the
+// compiler allocates the kernel's scalar registers, and the tile loop's walker
+// then moves to vector registers.
+__host__ __device__ inline void item_tile(int layout, bool causal, int nqblk, int ntq, int rows,
+                                          int blk, int r, int& qi, int& t) {
+  const int tc = ntq - 1 - r % ntq, qc = nqblk - 1 - r / ntq;  // contiguous
+  const int ts = ntq - 1 - r / nqblk, qs = nqblk - 1 - r % nqblk;  // striped
+  const int t1 = (blk >> 1) / rows;  // zigzag: tiles wholly inside the first chunk
+  const int n2 = ntq - t1;           // and tiles that reach the second chunk
+  const bool second = t1 == 0 || r < nqblk * n2;
+  const int r1 = r - nqblk * n2, t1d = t1 > 0 ? t1 : 1, n2d = n2 > 0 ? n2 : 1;
+  const int tz = second ? ntq - 1 - r % n2d : t1 - 1 - r1 % t1d;
+  const int qz = second ? r / n2d : nqblk - 1 - r1 / t1d;
+  const bool st = causal && layout == RA_STRIPED, zz = causal && layout == RA_ZIGZAG;
+  t = st ? ts : (zz ? tz : tc);
+  qi = st ? qs : (zz ? qz : qc);
+}
+
 // One launch of an attention kernel.  The query side is `nqblk` blocks of
 // `qlen` rows (block i belongs to device dev0 + i); the key side is `nkblk`
 // blocks of `klen` keys.  The query block of device p visits key blocks in
@@ -61,6 +128,33 @@ struct AttnParams {
 hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mode, bool state_io,
                             bool natural, hipStream_t s);
 bool mfma_supports(int D);
+// Rows per workgroup and resident workgroups per CU of the matrix-core kernel
+// for a query block of `qlen` rows.
+void mfma_geometry(int D, int qlen, int* rows, int* per_cu);
+// Device address, on the current device, of the XCD stamp array (nullptr on
+// failure).
+void* xcd_stat_address();
+
+// XCD split of a launch of `nwg` workgroups (ra_xcd.hip): fills *X and
+// returns the grid size.  `ring`: a whole-ring or one-device ring launch with
+// analytic positions, which is split by the measured XCD speeds; any other
+// launch keeps the fixed XCD-major order.  The plan is the kernel's second
+// argument: indexing a field of AttnParams by the XCD number would keep the
+// compiler from splitting AttnParams into scalars, and the tile loop's walker
+// then moves to vector registers.
+int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, int rows,
+                    int per_cu, hipStream_t s, XcdPlan* X);
+// After a successful launch prepared by xcd_prepare: read its stamps back now
+// and then (stream-ordered, into pinned host memory) to update the estimate.
+void xcd_after_launch(const XcdPlan& X, hipStream_t s);
+// The split xcd_prepare would use under per-XCD speeds `speeds` (host only):
+// fills *out and returns the grid size, or 0 when the launch is not split.
+int64_t xcd_plan_for(const AttnParams& p, int64_t nwg, bool causal, int rows, int per_cu,
+                     const float* speeds, XcdPlan* out);
+// The current device's speed estimate: read it (set = 0), fix it to `speeds`
+// (set = 1), or return to measuring from equal speeds (set = 1, speeds NULL).
+// Returns 0, -1 without a device, -2 for a speed that is not positive.
+int xcd_speeds(float* speeds, int* nmeas, int set);
 hipError_t launch_attn_valu(const AttnParams& p, int D, int dtype, bool causal, int pos_mode,
                             bool state_io, hipStream_t s);
 hipError_t launch_state_init(float* m, float* l, float* acc, int64_t rows, int64_t D,

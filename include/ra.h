@@ -19,7 +19,11 @@
  *
  * Conventions shared by every call
  *   - Every tensor and workspace is device memory owned by the caller.  The
- *     library never allocates, frees or keeps a pointer after a call returns.
+ *     library never allocates device memory, and never frees or keeps a
+ *     caller's pointer after a call returns.  Its only state is the XCD speed
+ *     estimate of ra_ring (see ra_xcd_speeds): a 128-byte array per GPU in the
+ *     library's own module and, set up once per device, 256 bytes of pinned
+ *     host memory and an event.
  *   - Tensors are dense and row-major with the head dim innermost:
  *       Q, out      [B, Hq,  Sq, D]      K, V   [B, Hkv, Sk, D]
  *       m, l, lse   [B, Hq,  Sq]  fp32   acc    [B, Hq,  Sq, D] fp32
@@ -168,6 +172,43 @@ ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int dev
  * entries).  Returns -1 (and sets ra_last_error) on invalid arguments, the
  * same checks as ra_positions. */
 int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64_t index);
+
+/* ---- Work split over the XCDs (not from the pages: a property of the GPU).
+ * An MI355X runs a launch on 8 XCDs (dies with their own L2); workgroup w goes
+ * to XCD w % 8.  The bf16 matrix-core ring kernel (ra_ring, D 32/64/128)
+ * numbers its work items XCD-major, longest first, and by default gives each
+ * XCD an equal share.  The XCDs of one GPU run a few percent apart, so ra_ring
+ * measures them: each launch with at least 64 items per XCD stamps when every
+ * XCD starts and ends (a 128-byte library array on the GPU), and the first 64
+ * launches on a device and then one in 8 copy the stamps, on the caller's
+ * stream, into pinned host memory that a later call reads once the copy has
+ * landed.  From the running speed estimate, a slow XCD hands the last (shortest)
+ * items of its list to faster ones when a simulation of the schedule says the
+ * launch ends sooner.  Results are the same bit for bit under any split.  The
+ * first such launch on a device sets up the stamp read-back (256 bytes of pinned
+ * host memory and an event, kept until the process ends); a launch inside a
+ * stream capture uses the current estimate and reads nothing back.  The
+ * environment variable RA_XCD_BALANCE=0 keeps the equal split. */
+
+/* The split ra_ring would use for this ring under per-XCD speeds speeds[8]
+ * (relative, any positive scale).  Host only.  plan receives 25 ints: M (items
+ * per XCD; XCD x owns items x*M .. x*M+M-1, longest first), keep[8], dbeg[8]
+ * and dcnt[8]: XCD x, slot by slot, first runs entries dbeg .. dbeg+dcnt-1 of
+ * the donated list (the items past every XCD's keep count, XCD after XCD),
+ * then its own first keep items; slot w / 8 of XCD w % 8 is workgroup w.
+ * Returns the grid size
+ * in workgroups, 0 when the launch is not split (plan is zeroed), or -1 (and
+ * sets ra_last_error) on invalid arguments, the same checks as ra_ring. */
+int64_t ra_xcd_plan(const ra_dims* d, int N, ra_layout layout, int causal, int device,
+                    const float* speeds, int* plan);
+
+/* The current device's per-XCD speed estimate (mean 1).  set == 0: copy it to
+ * speeds[8] and the number of measurements folded in to *nmeas (either may be
+ * NULL).  set == 1: fix the estimate to speeds[8] (normalised; not measured
+ * any more), or with speeds == NULL go back to equal speeds and measuring.
+ * RA_ERR_HIP without a current device, RA_ERR_SHAPE for a speed that is not
+ * positive and finite. */
+ra_status ra_xcd_speeds(float* speeds, int* nmeas, int set);
 
 /* Merge two states of the same rows built from disjoint key sets into `out`
  * ("Module 23", "The Math: One Block at a Time": the fold does not depend on

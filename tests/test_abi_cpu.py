@@ -9,6 +9,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from blockwise_online_softmax_amd import capi
 from blockwise_online_softmax_amd.capi import RaDims, RaState
@@ -41,7 +42,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert n in exported, f"{n} not exported"
         assert getattr(lib, n) is not None
-    assert lib.ra_version() == 104
+    assert lib.ra_version() == 105
 
 
 def dims(B=1, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, dtype=1, scale=0.0):
@@ -267,3 +268,87 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 8, 8)
     with pytest.raises(ValueError, match="GPU"):
         capi.ra_ring(x, x, x, x, torch.zeros(1, 1, 8), 1)
+
+
+# ---- work split over the XCDs (host planner) ----
+
+def _xcd_item(M, keep, dbeg, dcnt, w):
+    """Item of workgroup w under a plan, as include/ra.h describes the split."""
+    x, sl = w % 8, w // 8
+    if sl < dcnt[x]:  # donated items first
+        idx, y = dbeg[x] + sl, 0
+        while y < 7 and idx >= M - keep[y]:
+            idx -= M - keep[y]
+            y += 1
+        return y * M + keep[y] + idx
+    own = sl - dcnt[x]
+    return x * M + own if own < keep[x] else -1
+
+
+def _plan(B, Hq, Hkv, S, D, N, layout, causal, device=-1, speeds=None, dtype=torch.bfloat16):
+    Sq = S if device < 0 else S // N
+    q = torch.empty((B, Hq, Sq, D), dtype=dtype, device="meta")
+    k = torch.empty((B, Hkv, S, D), dtype=dtype, device="meta")
+    return capi.ra_xcd_plan(q, k, N, layout, causal, device, speeds)
+
+
+SKEW = [1.0, 0.97, 1.02, 0.96, 1.06, 0.99, 1.0, 0.95]
+
+
+@pytest.mark.parametrize("layout,causal,device", [
+    ("contiguous", True, -1), ("zigzag", True, -1), ("striped", True, -1),
+    ("contiguous", False, -1), ("zigzag", True, 0), ("zigzag", True, 5)])
+def test_xcd_plan_is_a_bijection(layout, causal, device):
+    S = 32768 if device < 0 else 262144
+    W = 32 * (S // 256) if device < 0 else 32 * (S // 8 // 256)
+    grid, M, keep, dbeg, dcnt = _plan(1, 32, 8, S, 128, 8, layout, causal, device, SKEW)
+    assert M * 8 == W and grid % 8 == 0
+    assert grid == 8 * max(k + c for k, c in zip(keep, dcnt))
+    items = [_xcd_item(M, keep, dbeg, dcnt, w) for w in range(grid)]
+    got = sorted(i for i in items if i >= 0)
+    assert got == list(range(W))
+    # an XCD's own items follow the ones it receives, in their longest-first
+    # order; an XCD that gives items away receives none
+    for x in range(8):
+        own = [items[(dcnt[x] + s) * 8 + x] for s in range(keep[x])]
+        assert own == [x * M + s for s in range(keep[x])]
+        assert keep[x] == M or dcnt[x] == 0
+
+
+def test_xcd_plan_equal_speeds_is_the_fixed_split():
+    grid, M, keep, dbeg, dcnt = _plan(1, 32, 8, 32768, 128, 8, "contiguous", True)
+    assert (grid, M) == (4096, 512)
+    assert keep == [512] * 8 and dcnt == [0] * 8
+
+
+def test_xcd_plan_moves_work_from_slow_to_fast():
+    grid, M, keep, dbeg, dcnt = _plan(1, 32, 8, 32768, 128, 8, "contiguous", True, -1, SKEW)
+    slow = [x for x in range(8) if SKEW[x] < 0.99]
+    fast = [x for x in range(8) if SKEW[x] > 1.01]
+    assert all(keep[x] < M for x in slow) and all(dcnt[x] == 0 for x in slow)
+    assert all(keep[x] == M for x in fast) and all(dcnt[x] > 0 for x in fast)
+    assert keep[7] < keep[3] < keep[1] < M  # slower XCDs give more away
+    assert dcnt[4] > dcnt[2]                # the fastest takes the most
+
+
+def test_xcd_plan_keeps_uniform_items():
+    # 16K tokens non-causal: every item is the same size, 8 per CU, so moving a
+    # few items would only lengthen some CU's list; the split stays fixed
+    grid, M, keep, dbeg, dcnt = _plan(1, 32, 32, 16384, 128, 8, "contiguous", False, -1, SKEW)
+    assert keep == [M] * 8 and dcnt == [0] * 8 and grid == 8 * M
+
+
+def test_xcd_plan_not_split():
+    # fewer than 64 items per XCD, fp32 inputs (vector kernel), head dim 16
+    assert _plan(1, 4, 2, 1024, 128, 4, "contiguous", True)[0] == 0
+    assert _plan(1, 32, 8, 32768, 128, 8, "contiguous", True, dtype=torch.float32)[0] == 0
+    assert _plan(1, 32, 8, 32768, 16, 8, "contiguous", True)[0] == 0
+
+
+def test_xcd_plan_rejects_bad_arguments():
+    with pytest.raises(ValueError, match="speeds"):
+        _plan(1, 32, 8, 32768, 128, 8, "contiguous", True, -1, [1, 1, 1, 0, 1, 1, 1, 1])
+    with pytest.raises(ValueError):
+        _plan(1, 32, 8, 32768, 128, 7, "contiguous", True)          # S % N != 0
+    with pytest.raises(ValueError):
+        _plan(1, 32, 8, 32768, 128, 8, "contiguous", True, device=8)
