@@ -155,20 +155,32 @@ def mfma_ceiling():
     return out
 
 
+KERNEL_SOURCES = ["blockwise_online_softmax_amd/csrc/ra_attn_mfma.hip",
+                  "blockwise_online_softmax_amd/csrc/ra_internal.h"]
+
+
+def kernel_sources_sha256():
+    """sha256 over the attention kernel's source files, in KERNEL_SOURCES order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def recorded_traffic(workload):
     """HBM bytes per launch of the attention kernel from the committed counter
     record (profiles/attn_mfma_<workload>_traffic.json), or None when there is
-    no record or the kernel source changed since the counters were taken."""
-    import hashlib
-
+    no record or the kernel's sources changed since the counters were taken."""
     path = os.path.join(HERE, "profiles", f"attn_mfma_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(os.path.join(HERE, rec["kernel_source"]), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if sha != rec["kernel_source_sha256"]:
+    if rec.get("kernel_sources") != KERNEL_SOURCES or \
+            rec.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
     return int(rec["hbm_bytes_per_launch"])
 

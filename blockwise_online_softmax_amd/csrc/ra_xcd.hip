@@ -34,7 +34,7 @@ constexpr int kCusPerXcd = 32;           // 256 CUs in 8 XCDs
 constexpr int kMinItems = 64;            // below this many items per XCD the split stays fixed
 constexpr int64_t kMaxItems = 1 << 22;   // bound on the planner's host work
 constexpr unsigned long long kMask40 = (1ull << 40) - 1;
-constexpr long long kMinTicks = 20000;   // launches shorter than 200 us are not measured
+constexpr long long kMinTicks = 100000;  // launches shorter than 1 ms are not measured
 constexpr int kMaxDev = 64;
 constexpr int kAvgN = 8;                 // measurements averaged (see consume)
 constexpr unsigned kReadAll = 64;        // launches read back one by one, then one in 8
@@ -296,7 +296,9 @@ void consume(DevState& d) {
     lo = std::min(lo, meas[x]);
     hi = std::max(hi, meas[x]);
   }
-  if (hi > 1.5 * lo) return;  // not a quiet launch (shared GPU, clock ramp)
+  // XCDs differ by a few percent; a wider spread means a launch that was not
+  // alone on the GPU, a clock ramp, or work too coarse for the model
+  if (hi > 1.25 * lo) return;
   // One launch's speeds scatter by a few percent around each XCD's own level:
   // the mean of the first kAvgN measurements, then a running average that
   // gives each new one a weight of 1 / kAvgN.

@@ -182,7 +182,8 @@ int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64
  * XCD starts and ends (a 128-byte library array on the GPU), and the first 64
  * launches on a device and then one in 8 copy the stamps, on the caller's
  * stream, into pinned host memory that a later call reads once the copy has
- * landed.  From the running speed estimate, a slow XCD hands the last (shortest)
+ * landed (launches of 1 ms or more are measured).  From the running speed
+ * estimate, a slow XCD hands the last (shortest)
  * items of its list to faster ones when a simulation of the schedule says the
  * launch ends sooner.  Results are the same bit for bit under any split.  The
  * first such launch on a device sets up the stamp read-back (256 bytes of pinned

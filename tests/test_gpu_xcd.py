@@ -39,7 +39,7 @@ def _inputs(B, Hq, Hkv, S, N, D, layout, device, seed):
 CASES = [  # (Hq, Hkv, S, N, layout, device)
     (16, 4, 8192, 8, "contiguous", -1),
     (16, 4, 8192, 8, "zigzag", -1),
-    (16, 4, 16384, 8, "striped", -1),
+    (16, 4, 65536, 8, "striped", 5),
     (16, 4, 65536, 8, "zigzag", 3),
 ]
 
