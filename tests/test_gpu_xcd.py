@@ -100,7 +100,9 @@ def test_split_launch_in_a_graph():
 
 
 def test_speed_estimate_is_measured():
-    B, Hq, Hkv, S, N, D = 1, 32, 8, 16384, 8, 128
+    # launches of about 8 ms: long enough to be measured (1 ms or more) and
+    # with enough work items per CU for the split's model
+    B, Hq, Hkv, S, N, D = 1, 32, 8, 32768, 8, 128
     log("xcd speed measurement")
     _, _, _, (q, k, v), _ = _inputs(B, Hq, Hkv, S, N, D, "contiguous", -1, 55)
     ra.ra_xcd_speeds(None, set=True)
