@@ -106,7 +106,7 @@ def test_speed_estimate_is_measured():
     log("xcd speed measurement")
     _, _, _, (q, k, v), _ = _inputs(B, Hq, Hkv, S, N, D, "contiguous", -1, 55)
     ra.ra_xcd_speeds(None, set=True)
-    for _ in range(24):
+    for _ in range(32):
         ra.ring_attention(q, k, v, N, "contiguous", True)
         torch.cuda.synchronize()
     speeds, nmeas = ra.ra_xcd_speeds()
