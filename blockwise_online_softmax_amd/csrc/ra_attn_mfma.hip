@@ -116,8 +116,8 @@ __device__ inline unsigned long long stamp40() {
 
 }  // namespace
 
-// XCD stamps of the ring launches (see XcdPlan); one copy per GPU.
-__device__ unsigned long long g_xcd_stat[2 * kXcds];
+// XCD stamps and busy times of the ring launches (see XcdPlan); one copy per GPU.
+__device__ unsigned long long g_xcd_stat[3 * kXcds];
 
 namespace {
 
@@ -271,7 +271,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   };
   static_assert(XPW * NW * 1024 == TILE_BYTES, "tile must split into 1 KB copies per wave");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TILE_BYTES];
+  // two buffers of K and V tiles, then 16 bytes: the workgroup's start stamp
+  // (placed last, so every tile offset stays the same)
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TILE_BYTES + 16];
   lds_t* smem = (lds_t*)smem_raw;  // generic -> LDS address space
 
   const int tid = threadIdx.x;
@@ -285,9 +287,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   const int64_t w = blockIdx.x;
   int64_t L = xcd_item(X, w);
   if (L < 0) return;  // a slot without an item (the whole workgroup)
+  unsigned long long* s_t0 = reinterpret_cast<unsigned long long*>(smem_raw + 2 * 2 * TILE_BYTES);
+  if (tid == 0) *s_t0 = stamp40();
   if (X.tag != 0 && w < kXcds && tid == 0) {  // the first workgroup of an XCD
     const int x = xcc_id();
     g_xcd_stat[x] = 0;
+    g_xcd_stat[2 * kXcds + x] = 0;
     g_xcd_stat[kXcds + x] = X.tag | stamp40();
   }
   const int G = P.Hq / P.Hkv;
@@ -758,7 +763,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   }
 
   // (no kernel argument is live across the tile loop for this)
-  if (tid == 0) atomicMax(&g_xcd_stat[xcc_id()], stamp40());
+  if (tid == 0) {
+    const unsigned long long t1 = stamp40();
+    const int x = xcc_id();
+    atomicMax(&g_xcd_stat[x], t1);
+    atomicAdd(&g_xcd_stat[2 * kXcds + x], (t1 - *s_t0) & ((1ull << 40) - 1));
+  }
 
   // ---- epilogue ----
   if (STATE_IO && mtrue > -__builtin_inff() && mtrue != m2) {  // move to the exact running max

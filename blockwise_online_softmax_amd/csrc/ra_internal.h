@@ -45,11 +45,12 @@ struct XcdPlan {
   int M;  // items per XCD; 0: no split (item = workgroup index)
   int keep[kXcds], dbeg[kXcds], dcnt[kXcds];
   // Non-zero: the launch is measured; bits 40..63 tag its start stamps.  Every
-  // workgroup of the matrix-core kernel raises its XCD's end stamp; the first
-  // workgroup of each XCD of a measured launch clears that end stamp and writes
-  // the tagged start stamp.  Stamps: the library's per-GPU array of 2 * 8
-  // values (xcd_stat_address), [x] end and [8 + x] start of XCD x, in 10 ns
-  // ticks of the GPU's constant clock (low 40 bits).
+  // workgroup of the matrix-core kernel raises its XCD's end stamp and adds its
+  // running time to its XCD's busy time; the first workgroup of each XCD of a
+  // measured launch clears both and writes the tagged start stamp.  Stamps: the
+  // library's per-GPU array of 3 * 8 values (xcd_stat_address): [x] end,
+  // [8 + x] start and [16 + x] busy time of XCD x, in 10 ns ticks of the GPU's
+  // constant clock (low 40 bits).
   unsigned long long tag;
 };
 

@@ -3,12 +3,13 @@
 //
 // The eight dies of one GPU do not run the ring kernel at the same speed (a few
 // percent apart per tile), so with an equal split the slowest die ends the
-// launch alone.  A planned launch stamps, per XCD, the start of its first
-// workgroup and the end of its last one.  The first 64 launches and then one in
-// 8 copy those stamps back on the caller's stream into pinned host memory; a
-// later call reads them once that copy has completed (never waiting for it).
-// The speed estimate they give, a running average, sizes the next launches'
-// split: a slow
+// launch alone.  A planned launch records, per XCD, the start of its first
+// workgroup, the end of its last one and the summed running time of its
+// workgroups.  The first 64 launches and then one in 8 copy those values back
+// on the caller's stream into pinned host memory; a later call reads them once
+// that copy has completed (never waiting for it).  Work over running time gives
+// each XCD's speed, and their running average sizes the next launches' split:
+// a slow
 // XCD hands the tail of its longest-first item list to faster ones, and the split
 // is kept only if a simulation of each XCD's list schedule says it ends sooner
 // than the fixed one.  Nothing here changes what any item computes.
@@ -30,6 +31,8 @@ namespace {
 
 constexpr int kTileKeys = 64;            // keys per tile of the matrix-core kernel
 constexpr double kItemFixed = 3.0;       // time of an item outside its tile loop, in tiles
+constexpr double kItemGap = 2.4;         // a CU's idle time between two workgroups, in tiles
+constexpr int kStatWords = 3 * kXcds;    // end stamps, start stamps, busy times
 constexpr int kCusPerXcd = 32;           // 256 CUs in 8 XCDs
 constexpr int kMinItems = 64;            // below this many items per XCD the split stays fixed
 constexpr int64_t kMaxItems = 1 << 22;   // bound on the planner's host work
@@ -97,17 +100,20 @@ std::vector<float> item_work(const Shape& s) {
 }
 
 // Finish time of a list of items taken in order by `slots` workgroup slots, each
-// taking the next item as soon as it is free.
-double makespan(const XcdPlan& X, const std::vector<float>& wk, int x, int slots) {
+// taking the next item as soon as it is free (with the CU's idle gap between
+// two workgroups); *work receives the list's total work.
+double makespan(const XcdPlan& X, const std::vector<float>& wk, int x, int slots, double* work) {
   std::priority_queue<double, std::vector<double>, std::greater<double>> q;
   for (int i = 0; i < slots; ++i) q.push(0.0);
   double end = 0;
+  *work = 0;
   for (int sl = 0; sl < X.keep[x] + X.dcnt[x]; ++sl) {
     const int64_t L = xcd_item(X, (int64_t)sl * kXcds + x);
-    const double t = q.top() + wk[(size_t)L];
+    const double t = q.top() + wk[(size_t)L] + kItemGap;
     q.pop();
     q.push(t);
     end = std::max(end, t);
+    *work += wk[(size_t)L];
   }
   return end;
 }
@@ -115,7 +121,8 @@ double makespan(const XcdPlan& X, const std::vector<float>& wk, int x, int slots
 struct Planned {
   XcdPlan xp;
   int64_t grid;
-  double ms[kXcds];  // simulated finish of each XCD, in tile units
+  double ms[kXcds];    // simulated finish of each XCD, in tile units
+  double work[kXcds];  // work of each XCD's items, in tile units
 };
 
 void fixed_plan(XcdPlan& X, int M) {
@@ -128,7 +135,7 @@ void fixed_plan(XcdPlan& X, int M) {
 double finish(Planned& P, const std::vector<float>& wk, const double* f, int slots) {
   double worst = 0;
   for (int x = 0; x < kXcds; ++x) {
-    P.ms[x] = makespan(P.xp, wk, x, slots);
+    P.ms[x] = makespan(P.xp, wk, x, slots, &P.work[x]);
     worst = std::max(worst, P.ms[x] / f[x]);
   }
   return worst;
@@ -218,7 +225,7 @@ struct DevState {
   unsigned calls = 0;                   // tag of the latest stamped launch
   bool pending = false;
   unsigned ptag = 0;
-  double pms[kXcds] = {};
+  double pwork[kXcds] = {};
   float f[kXcds] = {1, 1, 1, 1, 1, 1, 1, 1};  // speed estimate, mean 1
   int nmeas = 0;
   bool frozen = false;                  // set by the caller; not measured
@@ -246,7 +253,7 @@ void setup(DevState& d) {
   void* sym = xcd_stat_address();
   if (sym == nullptr) return;
   void* h = nullptr;
-  if (hipHostMalloc(&h, sizeof(unsigned long long) * 2 * kXcds, hipHostMallocDefault) !=
+  if (hipHostMalloc(&h, sizeof(unsigned long long) * kStatWords, hipHostMallocDefault) !=
       hipSuccess) {
     (void)hipGetLastError();
     return;
@@ -283,11 +290,14 @@ void consume(DevState& d) {
     if ((d.host[kXcds + x] >> 40) != tag) return;  // overlapped by another measured launch
     t0 = std::min(t0, (long long)(d.host[kXcds + x] & kMask40));
   }
+  // speed = the work of the XCD's items over the time its workgroups were
+  // running (the sum over its workgroups; idle CUs at the end do not count)
   double meas[kXcds], sum = 0;
   for (int x = 0; x < kXcds; ++x) {
     const long long dur = (long long)(d.host[x] & kMask40) - t0;
-    if (dur < kMinTicks) return;
-    meas[x] = d.pms[x] / (double)dur;
+    const double busy = (double)d.host[2 * kXcds + x];
+    if (dur < kMinTicks || !(busy > 0)) return;
+    meas[x] = d.pwork[x] / busy;
     sum += meas[x];
   }
   double lo = 1e300, hi = 0;
@@ -368,7 +378,7 @@ void xcd_after_launch(const XcdPlan& X, hipStream_t s) {
   DevState& d = g_dev[dev];
   const unsigned tag = (unsigned)(X.tag >> 40);
   if (!d.ok || d.pending || !(tag <= kReadAll || tag % 8 == 0)) return;
-  if (hipMemcpyAsync(d.host, d.stat, sizeof(unsigned long long) * 2 * kXcds,
+  if (hipMemcpyAsync(d.host, d.stat, sizeof(unsigned long long) * kStatWords,
                      hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipEventRecord(d.ev, s) != hipSuccess) {
     (void)hipGetLastError();
@@ -377,7 +387,7 @@ void xcd_after_launch(const XcdPlan& X, hipStream_t s) {
   }
   d.pending = true;
   d.ptag = tag;
-  memcpy(d.pms, d.plan.ms, sizeof d.pms);
+  memcpy(d.pwork, d.plan.work, sizeof d.pwork);
 }
 
 int64_t xcd_plan_for(const AttnParams& p, int64_t nwg, bool causal, int rows, int per_cu,

@@ -21,8 +21,8 @@
  *   - Every tensor and workspace is device memory owned by the caller.  The
  *     library never allocates device memory, and never frees or keeps a
  *     caller's pointer after a call returns.  Its only state is the XCD speed
- *     estimate of ra_ring (see ra_xcd_speeds): a 128-byte array per GPU in the
- *     library's own module and, set up once per device, 256 bytes of pinned
+ *     estimate of ra_ring (see ra_xcd_speeds): a 192-byte array per GPU in the
+ *     library's own module and, set up once per device, 192 bytes of pinned
  *     host memory and an event.
  *   - Tensors are dense and row-major with the head dim innermost:
  *       Q, out      [B, Hq,  Sq, D]      K, V   [B, Hkv, Sk, D]
@@ -179,14 +179,15 @@ int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64
  * numbers its work items XCD-major, longest first, and by default gives each
  * XCD an equal share.  The XCDs of one GPU run a few percent apart, so ra_ring
  * measures them: each launch with at least 64 items per XCD stamps when every
- * XCD starts and ends (a 128-byte library array on the GPU), and the first 64
+ * XCD starts and ends and how long its workgroups ran (a 192-byte library array
+ * on the GPU), and the first 64
  * launches on a device and then one in 8 copy the stamps, on the caller's
  * stream, into pinned host memory that a later call reads once the copy has
  * landed (launches of 1 ms or more are measured).  From the running speed
  * estimate, a slow XCD hands the last (shortest)
  * items of its list to faster ones when a simulation of the schedule says the
  * launch ends sooner.  Results are the same bit for bit under any split.  The
- * first such launch on a device sets up the stamp read-back (256 bytes of pinned
+ * first such launch on a device sets up the stamp read-back (192 bytes of pinned
  * host memory and an event, kept until the process ends); a launch inside a
  * stream capture uses the current estimate and reads nothing back.  The
  * environment variable RA_XCD_BALANCE=0 keeps the equal split. */
