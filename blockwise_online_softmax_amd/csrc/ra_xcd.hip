@@ -157,10 +157,10 @@ bool plan_valid(const XcdPlan& X, int64_t W, int64_t grid) {
 }
 
 // The split for per-XCD speeds fin (any positive scale): each XCD's target is
-// the total work times its share of the speed; an XCD above its target keeps the
-// head of its list up to the target, and the items it drops go, in order, to
-// the XCDs below theirs, which run them before their own.  Falls back to the fixed split unless the simulation
-// says the new one ends sooner.
+// the total work times its share of the speed; an XCD above its target keeps
+// the head of its list up to the target, and the items it drops go, in order,
+// to the XCDs below theirs, which run them before their own.  Falls back to the
+// fixed split unless the simulation says the new one ends sooner.
 Planned make_plan(const std::vector<float>& wk, int M, const float* fin, int slots) {
   double f[kXcds], fs = 0;
   for (int x = 0; x < kXcds; ++x) {
