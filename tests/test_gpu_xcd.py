@@ -36,18 +36,19 @@ def _inputs(B, Hq, Hkv, S, N, D, layout, device, seed):
     return q, k, v, [q[:, :, pos].contiguous().cuda(), kd.cuda(), vd.cuda()], pos
 
 
-CASES = [  # (Hq, Hkv, S, N, layout, device)
-    (16, 4, 8192, 8, "contiguous", -1),
-    (16, 4, 8192, 8, "zigzag", -1),
-    (16, 4, 65536, 8, "striped", 5),
-    (16, 4, 65536, 8, "zigzag", 3),
+CASES = [  # (B, Hq, Hkv, S, N, D, layout, device)
+    (1, 16, 4, 8192, 8, 128, "contiguous", -1),
+    (1, 16, 4, 8192, 8, 128, "zigzag", -1),
+    (1, 16, 4, 65536, 8, 128, "striped", 5),
+    (1, 16, 4, 65536, 8, 128, "zigzag", 3),
+    (2, 8, 2, 16384, 8, 64, "contiguous", -1),  # 4-wave kernel, two workgroups per CU
+    (2, 8, 2, 16384, 8, 32, "zigzag", -1),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[4]}_S{c[2]}_p{c[5]}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}_D{c[5]}_{c[6]}_S{c[3]}_p{c[7]}")
 def test_split_gives_identical_results(case):
-    Hq, Hkv, S, N, layout, device = case
-    B, D = 1, 128
+    B, Hq, Hkv, S, N, D, layout, device = case
     log(f"xcd split {case}")
     q, k, v, (qd, kd, vd), pos = _inputs(B, Hq, Hkv, S, N, D, layout, device, 77)
     grid, M, keep, dbeg, dcnt = ra.ra_xcd_plan(qd, kd, N, layout, True, device, SKEW)
