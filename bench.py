@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--vocab-ce", action="store_true",
                     help="vocab-parallel cross-entropy forward and gradient on 8192 rows x 128,256 "
                          "bf16 logits over 8 shards (HBM GB/s); one JSON line each")
+    ap.add_argument("--xcd-ab", action="store_true",
+                    help="the --workload ring with the even split over the 8 XCDs against the split "
+                         "sized by the measured XCD speeds (both frozen), alternating; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (contiguous ra_permute) so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -507,6 +510,58 @@ def tiny_latency(args):
                       "graph": "100 calls per graph, 10 replays"}), flush=True)
 
 
+def xcd_ab(args):
+    """The XCD split's effect on one workload, in one process: warm up with
+    measuring on, freeze the measured speeds, then time `steps` launches under
+    the even split and `steps` under the measured split, four times each, in
+    the order even-split, split-even, ... so that a drift of the GPU's speed
+    over the run cancels (HIP events around each launch)."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+    import workloads
+
+    wkey, layout, device = WORKLOADS[args.workload]
+    cfg = workloads.WORKLOADS[wkey]
+    print(f"# generating inputs for {args.workload}", file=sys.stderr, flush=True)
+    q, k, v = (t.cuda() for t in workloads.workload_inputs(wkey))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    nws = ra.ra_ring_workspace_bytes(q, k, cfg["N"], layout, device)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ra.ra_ring(q, k, v, out, lse, cfg["N"], layout, cfg["causal"], device, ws, stream=stream)
+
+    ra.ra_xcd_speeds(None, set=True)  # measure from equal speeds
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < max(args.warmup, 16) or time.perf_counter() - t_w < 1.0:
+        step()
+        torch.cuda.synchronize()
+        n_warm += 1
+    speeds, nmeas = ra.ra_xcd_speeds()
+    res = {"even": [], "split": []}
+    try:
+        for rep in range(4):
+            pair = (("even", [1.0] * 8), ("split", speeds))
+            for name, sp in (pair if rep % 2 == 0 else pair[::-1]):
+                ra.ra_xcd_speeds(sp, set=True)
+                res[name].append(timed(step, args.steps, 2, stream, stats=True)["mean"])
+    finally:
+        ra.ra_xcd_speeds(None, set=True)
+    grid, M, keep, dbeg, dcnt = ra.ra_xcd_plan(q, k, cfg["N"], layout, cfg["causal"], device, speeds)
+    even, split = float(np.mean(res["even"])), float(np.mean(res["split"]))
+    print(json.dumps({
+        "metric": "ring-attention launch ms, even split over the XCDs vs split by measured speed",
+        "workload": args.workload, "speeds": [round(x, 4) for x in speeds], "measurements": nmeas,
+        "warmup_calls": n_warm, "items_per_xcd": M, "items_moved": int(sum(dcnt)), "workgroups": grid,
+        "even_ms": [round(x, 4) for x in res["even"]], "split_ms": [round(x, 4) for x in res["split"]],
+        "gain": round(even / split - 1.0, 4),
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -533,6 +588,9 @@ def main():
         return
     if args.tiny:
         tiny_latency(args)
+        return
+    if args.xcd_ab:
+        xcd_ab(args)
         return
     if args.merge:
         merge_bench(args)
