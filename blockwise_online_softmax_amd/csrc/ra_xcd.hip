@@ -9,11 +9,11 @@
 // on the caller's stream into pinned host memory; a later call reads them once
 // that copy has completed (never waiting for it).  Work over running time gives
 // each XCD's speed, and their running average sizes the next launches' split:
-// a slow
-// XCD hands the tail of its longest-first item list to faster ones, and the split
-// is kept only if a simulation of each XCD's list schedule says it ends sooner
-// than the fixed one.  Nothing here changes what any item computes.
+// a slow XCD hands the tail of its longest-first item list to faster ones, and
+// the split is kept only if a simulation of each XCD's list schedule says it
+// ends sooner than the fixed one.  Nothing here changes what any item computes.
 #include <limits.h>
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -353,7 +353,10 @@ int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, in
     d.have_shape = true;
     d.have_plan = false;
   }
-  if (!d.have_plan || memcmp(d.pf, d.f, sizeof d.f) != 0) {
+  // replan when a speed has moved by more than 0.2 % since the plan was made
+  float moved = 0.f;
+  for (int x = 0; x < kXcds; ++x) moved = std::max(moved, std::fabs(d.pf[x] - d.f[x]));
+  if (!d.have_plan || moved > 0.002f) {
     d.plan = make_plan(d.wk, M, d.f, kCusPerXcd * per_cu);
     memcpy(d.pf, d.f, sizeof d.f);
     d.have_plan = true;
