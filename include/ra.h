@@ -178,29 +178,29 @@ int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64
  * to XCD w % 8.  The bf16 matrix-core ring kernel (ra_ring, D 32/64/128)
  * numbers its work items XCD-major, longest first, and by default gives each
  * XCD an equal share.  The XCDs of one GPU run a few percent apart, so ra_ring
- * measures them: each launch with at least 64 items per XCD stamps when every
+ * measures them.  Each launch with at least 64 items per XCD records when every
  * XCD starts and ends and how long its workgroups ran (a 192-byte library array
- * on the GPU), and the first 64
- * launches on a device and then one in 8 copy the stamps, on the caller's
- * stream, into pinned host memory that a later call reads once the copy has
- * landed (launches of 1 ms or more are measured).  From the running speed
- * estimate, a slow XCD hands the last (shortest)
- * items of its list to faster ones when a simulation of the schedule says the
- * launch ends sooner.  Results are the same bit for bit under any split.  The
- * first such launch on a device sets up the stamp read-back (192 bytes of pinned
- * host memory and an event, kept until the process ends); a launch inside a
- * stream capture uses the current estimate and reads nothing back.  The
- * environment variable RA_XCD_BALANCE=0 keeps the equal split. */
+ * on the GPU).  The first 64 launches on a device, then one in 8, copy that
+ * array on the caller's stream into pinned host memory, which a later call
+ * reads once the copy has landed; launches of 1 ms or more are measured.  From
+ * the running speed estimate, a slow XCD hands the last (shortest) items of its
+ * list to faster ones when a simulation of the schedule says the launch ends
+ * sooner.  Results are the same bit for bit under any split.  The first such
+ * launch on a device sets up the read-back (192 bytes of pinned host memory and
+ * an event, kept until the process ends); a launch inside a stream capture uses
+ * the current estimate and reads nothing back.  The environment variable
+ * RA_XCD_BALANCE=0 keeps the equal split. */
 
 /* The split ra_ring would use for this ring under per-XCD speeds speeds[8]
  * (relative, any positive scale).  Host only.  plan receives 25 ints: M (items
  * per XCD; XCD x owns items x*M .. x*M+M-1, longest first), keep[8], dbeg[8]
- * and dcnt[8]: XCD x, slot by slot, first runs entries dbeg .. dbeg+dcnt-1 of
+ * and dcnt[8].  XCD x, slot by slot, first runs entries dbeg .. dbeg+dcnt-1 of
  * the donated list (the items past every XCD's keep count, XCD after XCD),
  * then its own first keep items; slot w / 8 of XCD w % 8 is workgroup w.
- * Returns the grid size
- * in workgroups, 0 when the launch is not split (plan is zeroed), or -1 (and
- * sets ra_last_error) on invalid arguments, the same checks as ra_ring. */
+ * Returns the grid size in workgroups (8*M with keep = M and dcnt = 0 for the
+ * equal split); 0, with plan zeroed, for a launch that is never split (fewer
+ * than 64 items per XCD, or not the matrix-core kernel); -1 (and sets
+ * ra_last_error) on invalid arguments, the same checks as ra_ring. */
 int64_t ra_xcd_plan(const ra_dims* d, int N, ra_layout layout, int causal, int device,
                     const float* speeds, int* plan);
 
