@@ -336,13 +336,23 @@ int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, in
     (void)hipGetLastError();
     return nwg;
   }
+  // The launch runs on the stream's device.  Setup, copies and events act on
+  // the current device, so a launch on another device's stream uses that
+  // device's estimate but is not measured.
+  hipDevice_t sdev = dev;
+  if (s != nullptr &&
+      (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev < 0 || sdev >= kMaxDev)) {
+    (void)hipGetLastError();
+    return nwg;
+  }
+  const bool here = sdev == dev;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   const bool capturing =
       hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
   (void)hipGetLastError();
   std::lock_guard<std::mutex> lock(g_mu);
-  DevState& d = g_dev[dev];
-  if (!capturing) {  // no allocation, copy or event query inside a capture
+  DevState& d = g_dev[sdev];
+  if (!capturing && here) {  // no allocation, copy or event query inside a capture
     if (!d.tried) setup(d);
     if (d.pending) consume(d);
   }
@@ -362,7 +372,7 @@ int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, in
     d.have_plan = true;
   }
   *X = d.plan.xp;
-  if (d.ok && !capturing && !d.frozen) {
+  if (d.ok && !capturing && !d.frozen && here) {
     d.calls = (d.calls + 1) & 0xFFFFFF;
     if (d.calls == 0) d.calls = 1;
     X->tag = (unsigned long long)d.calls << 40;
