@@ -28,6 +28,9 @@ Modules:
              running states (m, l, o) or as finalized (out, lse).
   vocab_ce   O4: vocab-parallel cross-entropy (the page's three shard steps),
              the plain per-row definition and the gradient.
+  parallel   O1 run by a pool of CPU processes over row ranges (no arithmetic
+             of its own), for whole-output checks at full size and for the
+             CPU baseline.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, printed page values, library routines, brute force).  What no

@@ -20,6 +20,13 @@ A row that sees no key gets out_i = 0 and lse_i = -inf.
 
 Positions are global token positions (whatever the layout), so the causal
 rule is "key position <= query position", diagonal included.
+
+Causal rows are computed in chunks, and a chunk only meets the keys whose
+position is at most the chunk's last query position: every other key is
+masked for every row of the chunk and would add exactly zero ([M23] "Exact by
+Construction": the causal ring never computes blocks wholly in a device's
+future).  With keys in ascending position order that is a prefix of the key
+axis.
 """
 
 import numpy as np
@@ -39,6 +46,8 @@ def _as_f64(x):
 
 def _one_row_block(q_rows, k, v, visible, scale):
     """Rows q_rows [r, D] against keys k, v [Sk, D]; visible [r, Sk] bool or None."""
+    if k.shape[0] == 0:  # no key at all: every row is empty
+        return np.zeros((q_rows.shape[0], v.shape[1])), np.full(q_rows.shape[0], -np.inf)
     s = (q_rows @ k.T) * scale
     if visible is not None:
         s = np.where(visible, s, -np.inf)
@@ -70,6 +79,7 @@ def full_attention(q, k, v, q_pos=None, k_pos=None, causal=False, scale=None,
         scale = 1.0 / np.sqrt(D)
     qp = np.arange(Sq) if q_pos is None else np.asarray(q_pos, dtype=np.int64)
     kp = np.arange(Sk) if k_pos is None else np.asarray(k_pos, dtype=np.int64)
+    ascending = bool(np.all(np.diff(kp) >= 0))
     out = np.zeros((B, Hq, Sq, D))
     lse = np.zeros((B, Hq, Sq))
     for b in range(B):
@@ -77,8 +87,16 @@ def full_attention(q, k, v, q_pos=None, k_pos=None, causal=False, scale=None,
             g = h // G
             for r0 in range(0, Sq, row_chunk):
                 r1 = min(Sq, r0 + row_chunk)
-                vis = (kp[None, :] <= qp[r0:r1, None]) if causal else None
-                o, l_ = _one_row_block(q[b, h, r0:r1], k[b, g], v[b, g], vis, scale)
+                kk, vv, vis = k[b, g], v[b, g], None
+                if causal:
+                    last = qp[r0:r1].max()
+                    if ascending:  # the keys any row of the chunk can see: a prefix
+                        keys = slice(0, int(np.searchsorted(kp, last, side="right")))
+                    else:
+                        keys = np.flatnonzero(kp <= last)
+                    kk, vv = kk[keys], vv[keys]
+                    vis = kp[keys][None, :] <= qp[r0:r1, None]
+                o, l_ = _one_row_block(q[b, h, r0:r1], kk, vv, vis, scale)
                 out[b, h, r0:r1] = o
                 lse[b, h, r0:r1] = l_
     return out, lse

@@ -132,6 +132,17 @@ def pin_bruteforce(o):
                                               q_pos=qp, k_pos=kp, causal=causal, scale=scale)
         assert _maxdiff(out[0, 0], bo) < 1e-12
         assert _maxdiff(lse[0, 0], bl) < 1e-12
+        # row chunks of one and two rows, each meeting only the keys it can
+        # see (causal pruning), with keys in the given order and sorted by
+        # position
+        srt = np.argsort(kp, kind="stable")
+        for kk, vv, pp in ((k, v, kp), (k[srt], v[srt], kp[srt])):
+            for rc in (1, 2):
+                out, lse = o.attention.full_attention(q[None, None], kk[None, None],
+                                                      vv[None, None], q_pos=qp, k_pos=pp,
+                                                      causal=causal, scale=scale, row_chunk=rc)
+                assert _maxdiff(out[0, 0], bo) < 1e-12
+                assert _maxdiff(lse[0, 0], bl) < 1e-12
         ro, rl = o.attention.attention_rows(q[None, None], k[None, None], v[None, None],
                                             [(0, 0, i) for i in range(Sq)], q_pos=qp,
                                             k_pos=kp, causal=causal, scale=scale)

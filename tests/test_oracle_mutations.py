@@ -28,8 +28,12 @@ MUTATIONS = [
     ("ring.py", "g = h // G", "g = h % Hkv", "ring GQA head map"),
     ("ring.py", "out = np.where(pos[:, None], o / safe_l[:, None], 0.0)",
      "out = np.where(pos[:, None], o, 0.0)", "finalize skips division"),
-    ("attention.py", "vis = (kp[None, :] <= qp[r0:r1, None])", "vis = (kp[None, :] < qp[r0:r1, None])",
+    ("attention.py", "vis = kp[keys][None, :] <= qp[r0:r1, None]", "vis = kp[keys][None, :] < qp[r0:r1, None]",
      "full mask excludes diagonal"),
+    ("attention.py", 'np.searchsorted(kp, last, side="right")', 'np.searchsorted(kp, last, side="left")',
+     "causal key prefix drops the last visible key"),
+    ("attention.py", "keys = np.flatnonzero(kp <= last)", "keys = np.flatnonzero(kp < last)",
+     "causal key selection (unsorted keys) drops the last visible key"),
     ("attention.py", "scale = 1.0 / np.sqrt(D)\n    qp", "scale = 1.0 / D\n    qp", "wrong default scale"),
     ("attention.py", "g = h // G\n            for r0", "g = h % Hkv\n            for r0", "full GQA head map"),
     ("attention.py", "s = (q_rows @ k.T) * scale", "s = (q_rows @ k.T)", "scale dropped"),
