@@ -44,8 +44,9 @@
 //    the exact running max is tracked beside it and applied at the end;
 //  * only out and lse leave the kernel (whole ring): no row max is taken at
 //    all.  The exponentials use m2 as it stands, and a half-tile whose
-//    per-lane sum of p exceeds 2^64 (or is non-zero while m2 is still -inf)
-//    is redone after raising m2 to the row max, with l and o rescaled.
+//    per-lane sum of p exceeds 2^64 (and, for a real row, every half while
+//    m2 is still -inf) is redone after raising m2 to the row max, with l and
+//    o rescaled.
 //    out and lse do not depend on the reference.
 // Either way the rescale of o sits behind a wave-uniform branch that is
 // rarely taken.
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   int64_t L = xcd_item(X, w);
   if (L < 0) return;  // a slot without an item (the whole workgroup)
   unsigned long long* s_t0 = reinterpret_cast<unsigned long long*>(smem_raw + 2 * 2 * TILE_BYTES);
-  if (tid == 0) *s_t0 = stamp40();
+  if (X.tag != 0 && tid == 0) *s_t0 = stamp40();  // measured launches only
   if (X.tag != 0 && w < kXcds && tid == 0) {  // the first workgroup of an XCD
     const int x = xcc_id();
     g_xcd_stat[x] = 0;
@@ -362,10 +363,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   // Checked mode (the state does not leave the kernel, so only out and lse,
   // which do not depend on the reference, are produced): the exponentials use
   // the current reference m2 directly and no row max is taken; a half whose
-  // per-lane sum exceeds plim (p possibly above 2^kBig, or any p > 0 while
-  // m2 is still -inf) is redone after raising m2 to the row max.
-  float msub = 0.f;  // reference subtracted in the exponentials (0 while m2 = -inf)
-  float plim = 0.f;  // largest admitted per-lane sum of a half
+  // per-lane sum exceeds plim (p possibly above 2^kBig) is redone after
+  // raising m2 to the row max.  While m2 is still -inf, every half of a real
+  // row is redone (plim = -1): its visible scores may all be so negative that
+  // exp2 underflows to 0, and a zero sum must not pass for "nothing visible".
+  // A redo that finds no visible key leaves m2 at -inf.  Padding rows (past
+  // the query block) admit a zero sum, so their masked halves are not redone.
+  const float plim0 = rvalid ? -1.f : 0.f;  // plim while m2 = -inf
+  float msub = 0.f;    // reference subtracted in the exponentials (0 while m2 = -inf)
+  float plim = plim0;  // largest admitted per-lane sum of a half
   const int64_t srow = bh * P.Sq_tot + qrow;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -616,7 +622,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       const float alpha = raise ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.0f;
       m2 = mnew;
       msub = m2 > -__builtin_inff() ? m2 : 0.f;
-      plim = m2 > -__builtin_inff() ? __builtin_amdgcn_exp2f(kBig) : 0.f;
+      plim = m2 > -__builtin_inff() ? __builtin_amdgcn_exp2f(kBig) : plim0;
       ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -762,8 +768,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     }
   }
 
-  // (no kernel argument is live across the tile loop for this)
-  if (tid == 0) {
+  // measured launches: raise the XCD's end stamp, add this workgroup's time
+  if (X.tag != 0 && tid == 0) {
     const unsigned long long t1 = stamp40();
     const int x = xcc_id();
     atomicMax(&g_xcd_stat[x], t1);

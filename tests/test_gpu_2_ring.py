@@ -192,3 +192,78 @@ def test_score_jumps(layout, causal):
     ro, rl = O1.full_attention(q, k, v, causal=causal)
     assert float(np.max(rl)) > 40.0  # some rows meet scores far above their earlier tiles
     check(out, lse, ro, rl, torch.bfloat16, f"score jumps {layout} causal={causal}")
+
+
+def step_api_ring(q, k, v, N, layout):
+    """The same causal ring through ra_block_step (one call per block, ring
+    order, explicit positions) and ra_finalize; natural order in and out."""
+    B, Hq, S, D = q.shape
+    blk = S // N
+    qd, kd, vd = gpu(q, k, v)
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    for p in range(N):
+        qpos = OL.device_positions(S, N, layout, p)
+        qi = qd[:, :, qpos].contiguous()
+        st = ra.State(B, Hq, blk, D)
+        ra.ra_state_init(st)
+        qp = torch.from_numpy(qpos.astype(np.int32)).cuda()
+        for s in range(N):
+            j = (p - s) % N
+            kpos = OL.device_positions(S, N, layout, j)
+            kp = torch.from_numpy(kpos.astype(np.int32)).cuda()
+            ra.ra_block_step(qi, kd[:, :, kpos].contiguous(), vd[:, :, kpos].contiguous(), qp,
+                             kp, ra.RA_MASK_CAUSAL, st)
+        o = torch.empty_like(qi)
+        l_ = torch.empty((B, Hq, blk), dtype=torch.float32, device="cuda")
+        ra.ra_finalize(st, o, l_)
+        out[:, :, qpos] = o
+        lse[:, :, qpos] = l_
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.float32, 64)])
+def test_very_negative_scores(layout, dtype, D):
+    """Every score far below the exponential's range against a zero reference.
+
+    Part 1: q = -c * 1, k = 1 gives the constant score s = -c sqrt(D) ~ -120
+    (natural log), so exp(s) underflows in fp32 for every pair; the result is
+    still exact: out = mean of the visible value rows, lse = s + ln(#visible).
+    Part 2: random rows with q_0 = -c' k_0, so the first causal row's only
+    visible score is ~ -110.  The whole ring (which starts without a reference)
+    must agree with the oracle and with the step API (which takes row maxima)."""
+    B, Hq, Hkv, S, N = 1, 4, 2, 1024, 4
+    c = 10.625 if D == 128 else 13.25  # exact in bf16; s = -c * sqrt(D): -120.2, -106
+    q = torch.full((B, Hq, S, D), -c, dtype=torch.float32)
+    k = torch.ones((B, Hkv, S, D), dtype=torch.float32)
+    v = rand((B, Hkv, S, D), 71, torch.float32)
+    q, k, v = (t.to(dtype) for t in (q, k, v))
+    out, lse = run_ring(q, k, v, N, layout, True)
+    ro, rl = O1.full_attention(q, k, v, causal=True)
+    s = -c * np.sqrt(D)
+    assert s < -100
+    n = np.arange(1, S + 1)
+    assert np.allclose(rl[0, 0], s + np.log(n), atol=1e-9)  # the closed form, in the oracle too
+    check(out, lse, ro, rl, dtype, f"constant score {s:.1f} {layout} D={D}")
+    so, sl = step_api_ring(q, k, v, N, layout)
+    check(so, sl, ro, rl, dtype, f"constant score {s:.1f}, step API, {layout} D={D}")
+
+    q = rand((B, Hq, S, D), 72, torch.float32)
+    k = rand((B, Hkv, S, D), 73, torch.float32)
+    G = Hq // Hkv
+    k = k.to(dtype).float()
+    for h in range(Hq):
+        k0 = k[0, h // G, 0]
+        q[0, h, 0] = -(110.0 * np.sqrt(D) / float((k0 * k0).sum())) * k0
+    q, k = q.to(dtype), k.to(dtype)
+    out, lse = run_ring(q, k, v, N, layout, True)
+    ro, rl = O1.full_attention(q, k, v, causal=True)
+    assert float(rl[0, :, 0].max()) < -105
+    check(out, lse, ro, rl, dtype, f"single key at ~-110 {layout} D={D}")
+    so, sl = step_api_ring(q, k, v, N, layout)
+    check(so, sl, ro, rl, dtype, f"single key at ~-110, step API, {layout} D={D}")
+    eo = maxerr(to_np(out), to_np(so))
+    log(f"  whole ring vs step API: out {eo:.2e}")
