@@ -266,15 +266,18 @@ def ra_xcd_plan(q, k, N, layout, causal, device=-1, speeds=None, scale=None):
     return int(g), v[0], v[1:9], v[9:17], v[17:25]
 
 
-def ra_xcd_speeds(speeds=None, set=False):
-    """The current device's per-XCD speed estimate.  set=False: returns
-    (speeds, measurements).  set=True: fixes the estimate to `speeds` (no
-    more measuring), or with speeds=None returns to equal speeds and
-    measuring."""
+def ra_xcd_speeds(speeds=None, set=False, measure=False):
+    """The current device's per-XCD split.  Default: returns (speeds,
+    measurements) of the estimate.  set=True: split ra_ring launches by
+    `speeds` from now on, or with speeds=None equally (the library's default,
+    which touches no host state).  measure=True: measure the speeds from the
+    next launches on (each measured launch copies 192 bytes back on its
+    stream)."""
     sp = (ctypes.c_float * 8)(*([1.0] * 8 if speeds is None else [float(x) for x in speeds]))
     n = ctypes.c_int(0)
-    arg = None if (set and speeds is None) else sp
-    _check(load().ra_xcd_speeds(arg, ctypes.byref(n), int(bool(set))), "ra_xcd_speeds")
+    mode = 2 if measure else int(bool(set))
+    arg = None if (mode == 1 and speeds is None) else sp
+    _check(load().ra_xcd_speeds(arg, ctypes.byref(n), mode), "ra_xcd_speeds")
     return list(sp), int(n.value)
 
 

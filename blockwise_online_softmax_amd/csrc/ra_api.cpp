@@ -619,10 +619,11 @@ int64_t ra_xcd_plan(const ra_dims* d, int N, ra_layout layout, int causal, int d
 }
 
 ra_status ra_xcd_speeds(float* speeds, int* nmeas, int set) {
-  if (set != 0 && set != 1) return fail(RA_ERR_ENUM, "set must be 0 or 1 (got %d)", set);
+  if (set < 0 || set > 2) return fail(RA_ERR_ENUM, "set must be 0, 1 or 2 (got %d)", set);
   const int r = ra::xcd_speeds(speeds, nmeas, set);
   if (r == -1) return fail(RA_ERR_HIP, "no current HIP device");
   if (r == -2) return fail(RA_ERR_SHAPE, "speeds must be positive and finite");
+  if (r == -3) return fail(RA_ERR_HIP, "could not set up the read-back (pinned memory, event)");
   return ok();
 }
 

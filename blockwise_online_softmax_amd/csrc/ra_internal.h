@@ -45,9 +45,10 @@ struct XcdPlan {
   int M;  // items per XCD; 0: no split (item = workgroup index)
   int keep[kXcds], dbeg[kXcds], dcnt[kXcds];
   // Non-zero: the launch is measured; bits 40..63 tag its start stamps.  Every
-  // workgroup of the matrix-core kernel raises its XCD's end stamp and adds its
-  // running time to its XCD's busy time; the first workgroup of each XCD of a
-  // measured launch clears both and writes the tagged start stamp.  Stamps: the
+  // workgroup of a measured launch raises its XCD's end stamp and adds its
+  // running time to its XCD's busy time; the first workgroup of each XCD
+  // clears both and writes the tagged start stamp (a launch with tag 0 touches
+  // none of this).  Stamps: the
   // library's per-GPU array of 3 * 8 values (xcd_stat_address): [x] end,
   // [8 + x] start and [16 + x] busy time of XCD x, in 10 ns ticks of the GPU's
   // constant clock (low 40 bits).
@@ -138,23 +139,29 @@ void* xcd_stat_address();
 
 // XCD split of a launch of `nwg` workgroups (ra_xcd.hip): fills *X and
 // returns the grid size.  `ring`: a whole-ring or one-device ring launch with
-// analytic positions, which is split by the measured XCD speeds; any other
-// launch keeps the fixed XCD-major order.  The plan is the kernel's second
-// argument: indexing a field of AttnParams by the XCD number would keep the
-// compiler from splitting AttnParams into scalars, and the tile loop's walker
-// then moves to vector registers.
+// analytic positions, which is split by the device's fixed or measured XCD
+// speeds when its mode asks for it (xcd_speeds); any other launch, and every
+// launch in the default mode, keeps the fixed XCD-major order.  The plan is
+// the kernel's second argument: indexing a field of AttnParams by the XCD
+// number would keep the compiler from splitting AttnParams into scalars, and
+// the tile loop's walker then moves to vector registers.
 int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, int rows,
                     int per_cu, hipStream_t s, XcdPlan* X);
-// After a successful launch prepared by xcd_prepare: read its stamps back now
-// and then (stream-ordered, into pinned host memory) to update the estimate.
+// After a successful launch prepared by xcd_prepare: in measuring mode, read
+// its stamps back now and then (stream-ordered, into pinned host memory) to
+// update the estimate; otherwise nothing.
 void xcd_after_launch(const XcdPlan& X, hipStream_t s);
 // The split xcd_prepare would use under per-XCD speeds `speeds` (host only):
 // fills *out and returns the grid size, or 0 when the launch is not split.
 int64_t xcd_plan_for(const AttnParams& p, int64_t nwg, bool causal, int rows, int per_cu,
                      const float* speeds, XcdPlan* out);
-// The current device's speed estimate: read it (set = 0), fix it to `speeds`
-// (set = 1), or return to measuring from equal speeds (set = 1, speeds NULL).
-// Returns 0, -1 without a device, -2 for a speed that is not positive.
+// The current device's XCD split mode and speed estimate.  set = 0: read the
+// estimate; returns the mode (0 equal split, 1 fixed speeds, 2 measuring).
+// set = 1: split by `speeds` from now on, or equally with speeds NULL (the
+// default; launches then touch no host state).  set = 2: measure from equal
+// speeds (allocates the read-back on first use).  Returns 0 (set = 1, 2), -1
+// without a device, -2 for a speed that is not positive, -3 when the
+// read-back cannot be set up.
 int xcd_speeds(float* speeds, int* nmeas, int set);
 hipError_t launch_attn_valu(const AttnParams& p, int D, int dtype, bool causal, int pos_mode,
                             bool state_io, hipStream_t s);

@@ -1,15 +1,17 @@
-// Split of ring launches over the XCDs of the GPU, sized by each XCD's
-// measured speed.
+// Split of ring launches over the XCDs of the GPU, sized by per-XCD speeds.
 //
 // The eight dies of one GPU do not run the ring kernel at the same speed (a few
 // percent apart per tile), so with an equal split the slowest die ends the
-// launch alone.  A planned launch records, per XCD, the start of its first
-// workgroup, the end of its last one and the summed running time of its
-// workgroups.  The first 64 launches and then one in 8 copy those values back
-// on the caller's stream into pinned host memory; a later call reads them once
-// that copy has completed (never waiting for it).  Work over running time gives
-// each XCD's speed, and their running average sizes the next launches' split:
-// a slow XCD hands the tail of its longest-first item list to faster ones, and
+// launch alone.  By default every launch splits equally and this file does
+// nothing at launch time.  A caller can give the speeds (FIXED mode), or ask
+// for them to be measured (MEASURING mode): then a launch records, per XCD, the
+// start of its first workgroup, the end of its last one and the summed running
+// time of its workgroups; the first 64 launches and then one in 8 copy those
+// values back on the caller's stream into pinned host memory (set up when the
+// mode is chosen), and a later call reads them once that copy has completed
+// (never waiting for it).  Work over running time gives each XCD's speed, and
+// their running average sizes the next launches' split.  Under either mode a
+// slow XCD hands the tail of its longest-first item list to faster ones, and
 // the split is kept only if a simulation of each XCD's list schedule says it
 // ends sooner than the fixed one.  Nothing here changes what any item computes.
 #include <limits.h>
@@ -18,6 +20,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <mutex>
 #include <queue>
@@ -217,8 +220,14 @@ Planned make_plan(const std::vector<float>& wk, int M, const float* fin, int slo
   return fixed;
 }
 
+// Per device: how its ring launches are split.  EQUAL (the default) uses the
+// fixed XCD-major split and touches no host state; FIXED plans for speeds the
+// caller set; MEASURING records stamps and reads them back to estimate speeds.
+enum Mode : int { EQUAL = 0, FIXED = 1, MEASURING = 2 };
+
 struct DevState {
-  bool tried = false, ok = false;       // stamp buffer and read-back set up
+  Mode mode = EQUAL;
+  bool ok = false;                      // stamp buffer and read-back set up
   unsigned long long* stat = nullptr;   // this device's g_xcd_stat
   unsigned long long* host = nullptr;   // pinned copy of it
   hipEvent_t ev = nullptr;              // completes when the copy has landed
@@ -228,7 +237,6 @@ struct DevState {
   double pwork[kXcds] = {};
   float f[kXcds] = {1, 1, 1, 1, 1, 1, 1, 1};  // speed estimate, mean 1
   int nmeas = 0;
-  bool frozen = false;                  // set by the caller; not measured
   bool have_shape = false;
   Shape shape{};
   std::vector<float> wk;
@@ -239,35 +247,36 @@ struct DevState {
 
 std::mutex g_mu;
 DevState g_dev[kMaxDev];
+std::atomic<int> g_active{0};  // devices not in EQUAL mode
 
-bool balance_enabled() {
-  static const bool on = [] {
-    const char* e = getenv("RA_XCD_BALANCE");
-    return !(e != nullptr && e[0] == '0');
-  }();
-  return on;
-}
-
-void setup(DevState& d) {
-  d.tried = true;
+// Pinned host memory and an event for the read-back (once per device, with
+// that device current; kept until the process ends).
+bool setup(DevState& d) {
+  if (d.ok) return true;
   void* sym = xcd_stat_address();
-  if (sym == nullptr) return;
+  if (sym == nullptr) return false;
   void* h = nullptr;
   if (hipHostMalloc(&h, sizeof(unsigned long long) * kStatWords, hipHostMallocDefault) !=
       hipSuccess) {
     (void)hipGetLastError();
-    return;
+    return false;
   }
   hipEvent_t ev = nullptr;
   if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
     (void)hipGetLastError();
     (void)hipHostFree(h);
-    return;
+    return false;
   }
   d.stat = (unsigned long long*)sym;
   d.host = (unsigned long long*)h;
   d.ev = ev;
   d.ok = true;
+  return true;
+}
+
+void set_mode(DevState& d, Mode m) {
+  if ((d.mode == EQUAL) != (m == EQUAL)) g_active += m == EQUAL ? -1 : 1;
+  d.mode = m;
 }
 
 // Reads the stamps of the pending launch if its copy has landed.
@@ -283,7 +292,7 @@ void consume(DevState& d) {
     d.ok = false;
     return;
   }
-  if (d.frozen) return;
+  if (d.mode != MEASURING) return;
   const unsigned long long tag = d.ptag;
   long long t0 = LLONG_MAX;
   for (int x = 0; x < kXcds; ++x) {
@@ -330,15 +339,16 @@ int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, in
   if (nwg % kXcds != 0 || nwg / kXcds > INT_MAX) return nwg;
   const int M = (int)(nwg / kXcds);
   fixed_plan(*X, M);
-  if (!ring || !balance_enabled() || M < kMinItems || nwg > kMaxItems) return nwg;
+  // the default: every device splits equally, and nothing below runs
+  if (!ring || M < kMinItems || nwg > kMaxItems || g_active.load() == 0) return nwg;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
     (void)hipGetLastError();
     return nwg;
   }
-  // The launch runs on the stream's device.  Setup, copies and events act on
-  // the current device, so a launch on another device's stream uses that
-  // device's estimate but is not measured.
+  // The launch runs on the stream's device.  Copies and events act on the
+  // current device, so a launch on another device's stream uses that device's
+  // split but is not measured.
   hipDevice_t sdev = dev;
   if (s != nullptr &&
       (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev < 0 || sdev >= kMaxDev)) {
@@ -346,15 +356,15 @@ int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, in
     return nwg;
   }
   const bool here = sdev == dev;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  const bool capturing =
-      hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
-  (void)hipGetLastError();
   std::lock_guard<std::mutex> lock(g_mu);
   DevState& d = g_dev[sdev];
-  if (!capturing && here) {  // no allocation, copy or event query inside a capture
-    if (!d.tried) setup(d);
-    if (d.pending) consume(d);
+  if (d.mode == EQUAL) return nwg;
+  bool capturing = false;
+  if (d.mode == MEASURING) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    capturing = hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+    (void)hipGetLastError();
+    if (!capturing && here && d.pending) consume(d);  // no event query inside a capture
   }
   const Shape sh = shape_of(p, causal, rows, per_cu);
   if (!d.have_shape || !(sh == d.shape)) {
@@ -372,7 +382,7 @@ int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, in
     d.have_plan = true;
   }
   *X = d.plan.xp;
-  if (d.ok && !capturing && !d.frozen && here) {
+  if (d.mode == MEASURING && d.ok && !capturing && here) {
     d.calls = (d.calls + 1) & 0xFFFFFF;
     if (d.calls == 0) d.calls = 1;
     X->tag = (unsigned long long)d.calls << 40;
@@ -381,7 +391,7 @@ int64_t xcd_prepare(const AttnParams& p, int64_t nwg, bool causal, bool ring, in
 }
 
 void xcd_after_launch(const XcdPlan& X, hipStream_t s) {
-  if (X.tag == 0) return;
+  if (X.tag == 0) return;  // only measured launches (MEASURING mode) carry a tag
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
     (void)hipGetLastError();
@@ -390,7 +400,7 @@ void xcd_after_launch(const XcdPlan& X, hipStream_t s) {
   std::lock_guard<std::mutex> lock(g_mu);
   DevState& d = g_dev[dev];
   const unsigned tag = (unsigned)(X.tag >> 40);
-  if (!d.ok || d.pending || !(tag <= kReadAll || tag % 8 == 0)) return;
+  if (d.mode != MEASURING || !d.ok || d.pending || !(tag <= kReadAll || tag % 8 == 0)) return;
   if (hipMemcpyAsync(d.host, d.stat, sizeof(unsigned long long) * kStatWords,
                      hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipEventRecord(d.ev, s) != hipSuccess) {
@@ -423,23 +433,25 @@ int xcd_speeds(float* speeds, int* nmeas, int set) {
   }
   std::lock_guard<std::mutex> lock(g_mu);
   DevState& d = g_dev[dev];
-  if (set) {
+  if (set == 1 || set == 2) {
     double sum = 0;
+    const bool given = set == 1 && speeds != nullptr;
     for (int x = 0; x < kXcds; ++x) {
-      const float v = speeds ? speeds[x] : 1.f;
+      const float v = given ? speeds[x] : 1.f;
       if (!(v > 0.f) || v > 1e6f) return -2;
       sum += v;
     }
-    for (int x = 0; x < kXcds; ++x) d.f[x] = (float)((speeds ? speeds[x] : 1.f) * kXcds / sum);
-    d.frozen = speeds != nullptr;
+    if (set == 2 && !setup(d)) return -3;
+    for (int x = 0; x < kXcds; ++x) d.f[x] = (float)((given ? speeds[x] : 1.f) * kXcds / sum);
     d.nmeas = 0;
     d.pending = false;  // a copy in flight is dropped: its launch used other speeds
+    set_mode(d, set == 2 ? MEASURING : (given ? FIXED : EQUAL));
     return 0;
   }
   if (speeds)
     for (int x = 0; x < kXcds; ++x) speeds[x] = d.f[x];
   if (nmeas) *nmeas = d.nmeas;
-  return 0;
+  return d.mode;
 }
 
 }  // namespace ra

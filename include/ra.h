@@ -20,9 +20,10 @@
  * Conventions shared by every call
  *   - Every tensor and workspace is device memory owned by the caller.  The
  *     library never allocates device memory, and never frees or keeps a
- *     caller's pointer after a call returns.  Its only state is the XCD speed
- *     estimate of ra_ring (see ra_xcd_speeds): a 192-byte array per GPU in the
- *     library's own module and, set up once per device, 192 bytes of pinned
+ *     caller's pointer after a call returns.  Its only state is the per-device
+ *     XCD split of ra_ring, which by default is the equal split and holds
+ *     nothing; measuring it (ra_xcd_speeds) uses a 192-byte array per GPU in
+ *     the library's own module and, set up by that call, 192 bytes of pinned
  *     host memory and an event.
  *   - Tensors are dense and row-major with the head dim innermost:
  *       Q, out      [B, Hq,  Sq, D]      K, V   [B, Hkv, Sk, D]
@@ -177,19 +178,12 @@ int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64
  * An MI355X runs a launch on 8 XCDs (dies with their own L2); workgroup w goes
  * to XCD w % 8.  The bf16 matrix-core ring kernel (ra_ring, D 32/64/128)
  * numbers its work items XCD-major, longest first, and by default gives each
- * XCD an equal share.  The XCDs of one GPU run a few percent apart, so ra_ring
- * measures them.  Each launch with at least 64 items per XCD records when every
- * XCD starts and ends and how long its workgroups ran (a 192-byte library array
- * on the GPU).  The first 64 launches on a device, then one in 8, copy that
- * array on the caller's stream into pinned host memory, which a later call
- * reads once the copy has landed; launches of 1 ms or more are measured.  From
- * the running speed estimate, a slow XCD hands the last (shortest) items of its
- * list to faster ones when a simulation of the schedule says the launch ends
- * sooner.  Results are the same bit for bit under any split.  The first such
- * launch on a device sets up the read-back (192 bytes of pinned host memory and
- * an event, kept until the process ends); a launch inside a stream capture uses
- * the current estimate and reads nothing back.  The environment variable
- * RA_XCD_BALANCE=0 keeps the equal split. */
+ * XCD an equal share; ra_ring then keeps no host state, takes no lock and
+ * enqueues nothing but the kernel.  The XCDs of one GPU run a few percent
+ * apart, so a caller may ask for a split by per-XCD speeds, given or measured
+ * (ra_xcd_speeds): a slow XCD then hands the last (shortest) items of its list
+ * to faster ones when a simulation of the schedule says the launch ends
+ * sooner.  Results are the same bit for bit under any split. */
 
 /* The split ra_ring would use for this ring under per-XCD speeds speeds[8]
  * (relative, any positive scale).  Host only.  plan receives 25 ints: M (items
@@ -204,12 +198,25 @@ int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64
 int64_t ra_xcd_plan(const ra_dims* d, int N, ra_layout layout, int causal, int device,
                     const float* speeds, int* plan);
 
-/* The current device's per-XCD speed estimate (mean 1).  set == 0: copy it to
- * speeds[8] and the number of measurements folded in to *nmeas (either may be
- * NULL).  set == 1: fix the estimate to speeds[8] (normalised; not measured
- * any more), or with speeds == NULL go back to equal speeds and measuring.
- * RA_ERR_HIP without a current device, RA_ERR_SHAPE for a speed that is not
- * positive and finite. */
+/* The current device's XCD split.
+ *   set == 0: copy the speed estimate (mean 1) to speeds[8] and the number of
+ *     measurements folded in to *nmeas (either may be NULL).
+ *   set == 1: with speeds[8] (relative, positive and finite), split ra_ring
+ *     launches on this device by those speeds from now on; with speeds NULL,
+ *     split equally (the default).
+ *   set == 2: measure the speeds from equal ones on.  This call allocates, once
+ *     per device, 192 bytes of pinned host memory and an event (kept until the
+ *     process ends).  Each later ring launch of at least 64 items per XCD on
+ *     this device records when every XCD starts and ends and how long its
+ *     workgroups ran (a 192-byte library array on the GPU); the first 64 such
+ *     launches, then one in 8, copy that array on the caller's stream into the
+ *     pinned memory, which a later call reads once the copy has landed.
+ *     Launches of 1 ms or more count.  A launch inside a stream capture is
+ *     split by the current estimate and measures nothing.  Freeze the result
+ *     with set == 1 to stop measuring.
+ * RA_ERR_HIP without a current device or when the read-back cannot be set up,
+ * RA_ERR_SHAPE for a speed that is not positive and finite, RA_ERR_ENUM for
+ * another value of set. */
 ra_status ra_xcd_speeds(float* speeds, int* nmeas, int set);
 
 /* Merge two states of the same rows built from disjoint key sets into `out`

@@ -357,6 +357,7 @@ def test_xcd_plan_rejects_bad_arguments():
 def test_xcd_speeds_error_paths(lib):
     sp = (ctypes.c_float * 8)(*([1.0] * 8))
     n = ctypes.c_int(0)
-    expect(lib.ra_xcd_speeds(sp, ctypes.byref(n), 2), capi.RA_ERR_ENUM, "set must be 0 or 1")
+    expect(lib.ra_xcd_speeds(sp, ctypes.byref(n), 3), capi.RA_ERR_ENUM, "set must be 0, 1 or 2")
+    expect(lib.ra_xcd_speeds(sp, ctypes.byref(n), -1), capi.RA_ERR_ENUM, "set must be 0, 1 or 2")
     if torch.cuda.device_count() == 0:  # reading or setting the estimate needs a device
         expect(lib.ra_xcd_speeds(sp, ctypes.byref(n), 0), capi.RA_ERR_HIP, "no current HIP device")

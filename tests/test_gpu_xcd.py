@@ -106,11 +106,21 @@ def test_speed_estimate_is_measured():
     B, Hq, Hkv, S, N, D = 1, 32, 8, 32768, 8, 128
     log("xcd speed measurement")
     _, _, _, (q, k, v), _ = _inputs(B, Hq, Hkv, S, N, D, "contiguous", -1, 55)
+    # the default mode measures nothing
     ra.ra_xcd_speeds(None, set=True)
-    for _ in range(32):
+    for _ in range(4):
         ra.ring_attention(q, k, v, N, "contiguous", True)
         torch.cuda.synchronize()
     speeds, nmeas = ra.ra_xcd_speeds()
+    assert nmeas == 0 and speeds == [1.0] * 8
+    try:
+        ra.ra_xcd_speeds(measure=True)
+        for _ in range(32):
+            ra.ring_attention(q, k, v, N, "contiguous", True)
+            torch.cuda.synchronize()
+        speeds, nmeas = ra.ra_xcd_speeds()
+    finally:
+        ra.ra_xcd_speeds(None, set=True)
     log(f"  speeds {[round(x, 4) for x in speeds]} from {nmeas} measurements")
     assert nmeas >= 1
     assert abs(sum(speeds) / 8 - 1.0) < 1e-3
