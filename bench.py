@@ -66,6 +66,46 @@ def sum_range(lo, hi):
     return (lo + hi) * (hi - lo + 1) // 2
 
 
+def layout_pos(layout, N, blk, dev, a):
+    """Global position of local index a (array) on device dev."""
+    a = np.asarray(a, dtype=np.int64)
+    if layout == "striped":
+        return dev + a * N
+    if layout == "zigzag":
+        c = blk // 2
+        return np.where(a < c, dev * c + a, (2 * N - 1 - dev) * c + (a - c))
+    return dev * blk + a
+
+
+def executed_pairs(S, N, layout, causal, device, D, tile_keys=64):
+    """(query, key) pairs the matrix-core ring kernel computes per query head,
+    masked ones included: every (query tile, key tile) it visits in full.  A
+    query tile is 256 rows (D = 128 and blocks of >= 256 rows) or 128; key
+    tiles are 64 keys.  Positions ascend inside a device block, so under the
+    causal mask a key block is skipped when its first key follows the tile's
+    last query, and otherwise runs up to its last tile that starts at or
+    before that query.  The excess over the visible pairs is the work done on
+    masked parts of diagonal tiles."""
+    blk = S // N
+    rows = 256 if (D == 128 and blk >= 256) else 128
+    devs = range(N) if device < 0 else [device]
+    ntile = -(-blk // tile_keys)
+    tile_first = np.arange(ntile) * tile_keys
+    total = 0
+    for p in devs:
+        for a0 in range(0, blk, rows):
+            nr = min(rows, blk - a0)
+            qmax = int(layout_pos(layout, N, blk, p, a0 + nr - 1)) if causal else None
+            for j in range(N):
+                if not causal:
+                    n = ntile
+                else:
+                    firsts = layout_pos(layout, N, blk, j, tile_first)
+                    n = int((firsts <= qmax).sum())
+                total += nr * n * tile_keys
+    return total
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +129,9 @@ def parse():
     ap.add_argument("--vocab-ce", action="store_true",
                     help="vocab-parallel cross-entropy forward and gradient on 8192 rows x 128,256 "
                          "bf16 logits over 8 shards (HBM GB/s); one JSON line each")
+    ap.add_argument("--xcd", choices=("measured", "equal"), default="measured",
+                    help="split of the ring launch over the 8 XCDs: by speeds measured during "
+                         "the warm-up and then frozen (default), or equal")
     ap.add_argument("--xcd-ab", action="store_true",
                     help="the --workload ring with the even split over the 8 XCDs against the split "
                          "sized by the measured XCD speeds (both frozen), alternating; one JSON line")
@@ -188,58 +231,66 @@ def recorded_traffic(workload):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def blas_threads():
-    try:
-        from threadpoolctl import threadpool_info
-
-        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:
-        return 1
-
-
 def cpu_baseline(q, k, v, cfg, layout, device, seconds, gpu_out=None, gpu_lse=None):
-    """Oracle (fp64 numpy) on a growing seeded row sample until `seconds` pass."""
-    import oracle
+    """The oracle (O1, fp64 numpy) on a bounded seeded sample of the same
+    workload, run by its process pool: one worker per allowed core (at most
+    16), one BLAS thread each, causal rows meeting only the keys they can
+    see.  Tasks are 64-row ranges of (head, rows) drawn in a seeded random
+    order, handed out until `seconds` have passed.  The rate is the
+    algorithmic FLOPs of the rows done over the pool's time (the upcast of the
+    inputs and the start of the workers are not counted); the time of the
+    whole workload is extrapolated from it."""
     from oracle import layouts as OL
-    import workloads
+    from oracle import parallel as OP
 
     S, N, D, Hq = cfg["S"], cfg["N"], cfg["D"], cfg["Hq"]
     Sq = q.shape[2]
     causal = cfg["causal"]
     if device >= 0:
-        qpos_all = OL.device_positions(S, N, layout, device)
-        kpos_all = OL.permuted_positions(S, N, layout)
+        # keys in natural order (the oracle works on positions, so reordering
+        # keys together with their positions changes nothing)
+        qpos = OL.device_positions(S, N, layout, device)
+        kpos = OL.permuted_positions(S, N, layout)
+        order = np.argsort(kpos, kind="stable")
+        k, v, kpos = k[:, :, order], v[:, :, order], kpos[order]
     else:
-        qpos_all, kpos_all = np.arange(S), np.arange(S)
-    rows_done, pairs, t_used = 0, 0, 0.0
+        qpos, kpos = np.arange(S), np.arange(S)
+    rows_per_task = 64
+    tasks = [(0, h, r0, min(Sq, r0 + rows_per_task)) for h in range(Hq)
+             for r0 in range(0, Sq, rows_per_task)]
+    rng = np.random.default_rng(1000)
+    tasks = [tasks[i] for i in rng.permutation(len(tasks))]
+    out, lse, info = OP.full_attention_pool(q, k, v, q_pos=qpos, k_pos=kpos, causal=causal,
+                                            tasks=tasks, sort_tasks=False, time_budget=seconds)
+    kp_sorted = np.sort(kpos)
+
+    def row_pairs(r0, r1):  # visible keys of rows r0..r1-1, summed
+        if not causal:
+            return (r1 - r0) * len(kpos)
+        return int(np.searchsorted(kp_sorted, qpos[r0:r1], side="right").sum())
+
+    pairs = sum(row_pairs(r0, r1) for _, _, r0, r1 in info["tasks_done"])
+    all_pairs = Hq * row_pairs(0, Sq)
     errs = [0.0, 0.0]
-    seed = 1000
-    while t_used < seconds and rows_done < Sq * Hq:
-        sample = workloads.sample_rows(Hq, Sq, 1, seed)
-        seed += 1
-        rows = [(0, h, i) for (h, i) in sample]
-        t0 = time.perf_counter()
-        out, lse = oracle.attention_rows(q, k, v, rows, q_pos=qpos_all, k_pos=kpos_all,
-                                         causal=causal)
-        t_used += time.perf_counter() - t0
-        rows_done += len(rows)
-        for (_, h, i) in rows:
-            pairs += int(qpos_all[i]) + 1 if causal and device < 0 else (
-                int((kpos_all <= qpos_all[i]).sum()) if causal else len(kpos_all))
-        if gpu_out is not None:
-            for n, (_, h, i) in enumerate(rows):
-                go = gpu_out[0, h, i].float().numpy()
-                errs[0] = max(errs[0], float(np.abs(go - out[n]).max()))
-                errs[1] = max(errs[1], abs(float(gpu_lse[0, h, i]) - lse[n]))
+    if gpu_out is not None:
+        for _, h, r0, r1 in info["tasks_done"]:
+            go = gpu_out[0, h, r0:r1].float().numpy()
+            errs[0] = max(errs[0], float(np.abs(go - out[0, h, r0:r1]).max()))
+            errs[1] = max(errs[1], float(np.abs(gpu_lse[0, h, r0:r1].numpy() - lse[0, h, r0:r1]).max()))
+    rate = pairs / info["seconds"]
     flops = 4.0 * D * pairs
     return {
-        "value": flops / t_used / 1e12,
+        "value": flops / info["seconds"] / 1e12,
         "unit": "TFLOP/s",
-        "cores": blas_threads(),
+        "cores": info["workers"],
         "kind": "oracle",
-        "sample": f"{rows_done} seeded (head, row) pairs of the same workload, fp64 numpy, "
-                  f"{t_used:.1f} s; {pairs} visible pairs",
+        "sample": f"{info['rows']} of {Hq * Sq} (head, row) outputs of the same workload "
+                  f"({len(info['tasks_done'])} seeded 64-row ranges), fp64 numpy O1, "
+                  f"{info['workers']} worker processes x 1 BLAS thread, {info['seconds']:.1f} s, "
+                  f"{pairs} visible pairs",
+        "cpu_model": info["cpu_model"],
+        "pool_seconds": round(info["seconds"], 2),
+        "full_workload_seconds_extrapolated": round(all_pairs / rate, 1),
     }, errs
 
 
@@ -534,7 +585,7 @@ def xcd_ab(args):
     def step():
         ra.ra_ring(q, k, v, out, lse, cfg["N"], layout, cfg["causal"], device, ws, stream=stream)
 
-    ra.ra_xcd_speeds(None, set=True)  # measure from equal speeds
+    ra.ra_xcd_speeds(measure=True)  # measure from equal speeds
     t_w = time.perf_counter()
     n_warm = 0
     while n_warm < max(args.warmup, 16) or time.perf_counter() - t_w < 1.0:
@@ -617,14 +668,26 @@ def main():
         ra.ra_ring(qd, kd, vd, out, lse, N, layout, causal, device, ws, stream=stream)
 
     # warm-up: `warmup` calls, then more until 0.5 s have passed (the shader
-    # clock ramps under load, and the XCD speed estimate averages 8 launches);
-    # synchronised, so each launch's XCD stamps land before the next call
+    # clock ramps under load).  With --xcd measured, the warm-up launches
+    # measure the XCD speeds (synchronised, so each launch's stamps land
+    # before the next call), and the split is then frozen: the timed launches
+    # enqueue the kernel and nothing else.
+    if args.xcd == "measured":
+        ra.ra_xcd_speeds(measure=True)
+    else:
+        ra.ra_xcd_speeds(None, set=True)
     t_w = time.perf_counter()
     n_warm = 0
     while n_warm < args.warmup or time.perf_counter() - t_w < 0.5:
         step()
         torch.cuda.synchronize()
         n_warm += 1
+    speeds, nmeas = ra.ra_xcd_speeds()
+    if args.xcd == "measured":
+        ra.ra_xcd_speeds(speeds, set=True)  # freeze
+    for _ in range(2):  # first launches under the frozen split
+        step()
+    torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -644,11 +707,11 @@ def main():
     q_tokens = qd.shape[2]
     props = torch.cuda.get_device_properties(0)
 
-    speeds, nmeas = ra.ra_xcd_speeds()
     grid, M, keep, dbeg, dcnt = ra.ra_xcd_plan(qd, kd, N, layout, causal, device, speeds)
-    xcd = {"speeds": [round(x, 4) for x in speeds], "measurements": nmeas,
-           "workgroups": grid, "items_per_xcd": M, "items_moved": int(sum(dcnt)),
-           "balance": os.environ.get("RA_XCD_BALANCE", "1") != "0"}
+    xcd = {"mode": args.xcd, "speeds": [round(x, 4) for x in speeds], "measurements": nmeas,
+           "workgroups": grid, "items_per_xcd": M, "items_moved": int(sum(dcnt))}
+    ra.ra_xcd_speeds(None, set=True)
+    exec_flops = 4.0 * D * cfg["B"] * Hq * executed_pairs(S, N, layout, causal, device, D)
     ceiling = mfma_ceiling()
     ceiling["attention_kernel_frac_of_ceiling"] = round(kern_tflops / ceiling["tflops"], 4)
     cpu = None
@@ -680,6 +743,8 @@ def main():
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(q_tokens / (ms_per_step * 1e-3), 1),
         "algorithmic_tflop": round(flops / 1e12, 4),
+        "executed_tflop": round(exec_flops / 1e12, 4),
+        "executed_over_algorithmic": round(exec_flops / flops, 4),
         "roofline": {
             "bound": "mfma", "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),

@@ -115,7 +115,8 @@ def _fill_f64(dst, x):
 
 def full_attention_pool(q, k, v, q_pos=None, k_pos=None, causal=False, scale=None,
                         workers=None, rows_per_task=1024, row_chunk=64, tasks=None,
-                        progress=None, progress_every=20.0, time_budget=None):
+                        progress=None, progress_every=20.0, time_budget=None,
+                        sort_tasks=True):
     """oracle.attention.full_attention, computed by a pool of processes.
 
     q [B, Hq, Sq, D], k, v [B, Hkv, Sk, D] (torch tensors or arrays, any float
@@ -124,6 +125,7 @@ def full_attention_pool(q, k, v, q_pos=None, k_pos=None, causal=False, scale=Non
     them are left as NaN.  progress(done_rows, total_rows, seconds) is called
     at most every `progress_every` seconds.  time_budget: stop handing out
     tasks once that many seconds have passed (the tasks in flight finish).
+    sort_tasks: hand out causal tasks longest first (else in the given order).
 
     Returns (out [B, Hq, Sq, D], lse [B, Hq, Sq], info) with out and lse
     float64 and info = {"workers", "seconds", "rows", "tasks_done", "cpu_model"};
@@ -144,7 +146,7 @@ def full_attention_pool(q, k, v, q_pos=None, k_pos=None, causal=False, scale=Non
                  for b in range(B) for h in range(Hq) for r0 in range(0, Sq, rows_per_task)]
     # the longest ranges first (under a causal mask, those with the latest
     # positions), so the pool ends evenly
-    if causal:
+    if causal and sort_tasks:
         tasks = sorted(tasks, key=lambda t: -int(qp[t[2]:t[3]].max()))
     sh = _Shared(8 * (2 * B * Hq * Sq * D + 2 * B * Hkv * Sk * D + 2 * B * Hq * Sq + Sq + Sk))
     try:
