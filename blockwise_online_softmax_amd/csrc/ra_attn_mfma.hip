@@ -105,6 +105,14 @@ __device__ inline void dma16(const void* src, lds_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int n = bytes >= 0xFFFFFFFFll ? (int)0xFFFFFFFFu : (int)(uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ inline void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, lds_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
+}
 __device__ inline void wait_dma() {
   // vmcnt(0); expcnt and lgkmcnt left at their maxima (no wait)
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -161,7 +169,10 @@ struct Tile {
   int kp;
 };
 
-template <bool CAUSAL, int POS, bool NAT>
+// LAY: the layout when fixed at compile time (RA_CONTIGUOUS, RA_STRIPED,
+// RA_ZIGZAG), or -1 to read it from the parameters.  A fixed layout turns the
+// walker's position arithmetic into a few scalar instructions per tile.
+template <bool CAUSAL, int POS, bool NAT, int LAY = -1>
 struct TileWalker {
   int s, tt, j;
   bool bfull;
@@ -178,13 +189,14 @@ struct TileWalker {
   // Advance to the next tile with at least one visible pair.
   __device__ bool next(const AttnParams& P, int dev, int qmin, int qmax, Tile& T) {
     const int lane = threadIdx.x & 63;
+    const int lay = LAY >= 0 ? LAY : P.layout;
     while (s < P.nkblk) {
       if (tt == 0) {
         j = ((dev - s) % P.nkblk + P.nkblk) % P.nkblk;  // ring order
         bfull = !CAUSAL;
         if (CAUSAL && POS == POS_ANALYTIC) {
-          const int kf = layout_pos(P.layout, P.N, P.blk, j, 0);
-          const int kl = layout_pos(P.layout, P.N, P.blk, j, P.klen - 1);
+          const int kf = layout_pos(lay, P.N, P.blk, j, 0);
+          const int kl = layout_pos(lay, P.N, P.blk, j, P.klen - 1);
           if (kf > qmax) {
             ++s;
             continue;
@@ -205,22 +217,22 @@ struct TileWalker {
       bool full = (n == BN);
       if (NAT && !(CAUSAL && POS == POS_ANALYTIC)) {
         // natural-order rows: position of the tile's keys (no mask needed)
-        T.p0 = layout_pos(P.layout, P.N, P.blk, j, a0);
-        T.stride = P.layout == RA_STRIPED ? P.N : 1;
+        T.p0 = layout_pos(lay, P.N, P.blk, j, a0);
+        T.stride = lay == RA_STRIPED ? P.N : 1;
         T.split = BN;
         T.p1 = T.p0;
-        if (P.layout == RA_ZIGZAG) {
+        if (lay == RA_ZIGZAG) {
           const int c = P.blk >> 1;
           if (a0 < c && a0 + n > c) {
             T.split = c - a0;
-            T.p1 = layout_pos(P.layout, P.N, P.blk, j, c) - (c - a0);
+            T.p1 = layout_pos(lay, P.N, P.blk, j, c) - (c - a0);
           }
         }
       }
       if (CAUSAL && POS == POS_ANALYTIC) {
-        const int kf = layout_pos(P.layout, P.N, P.blk, j, a0);
+        const int kf = layout_pos(lay, P.N, P.blk, j, a0);
         if (!bfull) {
-          const int kl = layout_pos(P.layout, P.N, P.blk, j, a0 + n - 1);
+          const int kl = layout_pos(lay, P.N, P.blk, j, a0 + n - 1);
           if (kf > qmax) {  // positions ascend in a block: nothing after is visible
             ++s;
             tt = 0;
@@ -228,15 +240,15 @@ struct TileWalker {
           }
           full = full && (kl <= qmin);
         }
-        T.stride = P.layout == RA_STRIPED ? P.N : 1;
+        T.stride = lay == RA_STRIPED ? P.N : 1;
         T.p0 = kf;
         T.split = BN;
         T.p1 = kf;
-        if (P.layout == RA_ZIGZAG) {
+        if (lay == RA_ZIGZAG) {
           const int c = P.blk >> 1;
           if (a0 < c && a0 + n > c) {
             T.split = c - a0;
-            T.p1 = layout_pos(P.layout, P.N, P.blk, j, c) - (c - a0);
+            T.p1 = layout_pos(lay, P.N, P.blk, j, c) - (c - a0);
           }
         }
       }
@@ -256,7 +268,7 @@ struct TileWalker {
   }
 };
 
-template <int D, int NW, bool CAUSAL, int POS, bool STATE_IO, bool NAT = false>
+template <int D, int NW, bool CAUSAL, int POS, bool STATE_IO, bool NAT = false, int LAY = -1>
 __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, XcdPlan X) {
   constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
   constexpr int NDB = D / 32;         // 32-row d blocks of O^T
@@ -277,6 +289,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TILE_BYTES + 16];
   lds_t* smem = (lds_t*)smem_raw;  // generic -> LDS address space
 
+  const int lay = LAY >= 0 ? LAY : P.layout;  // the layout (a constant when LAY >= 0)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index, uniform across the wave (kept in a scalar register)
@@ -301,7 +314,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   L /= G;
   const int nt = P.nqblk * P.ntq;
   int qi, t;
-  item_tile(P.layout, CAUSAL && POS == POS_ANALYTIC, P.nqblk, P.ntq, NW * 32, P.blk,
+  item_tile(lay, CAUSAL && POS == POS_ANALYTIC, P.nqblk, P.ntq, NW * 32, P.blk,
             (int)(L % nt), qi, t);
   L /= nt;
   const int g = (int)(L % P.Hkv);
@@ -317,7 +330,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   // token position
   int64_t qrow;
   if constexpr (NAT)
-    qrow = rvalid ? layout_pos(P.layout, P.N, P.blk, dev, la) : 0;
+    qrow = rvalid ? layout_pos(lay, P.N, P.blk, dev, la) : 0;
   else
     qrow = (int64_t)qi * P.qlen + la;
   const int64_t bh = (int64_t)b * P.Hq + h;
@@ -340,9 +353,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   int qpos = 0, qmin = 0, qmax = 0;
   if (CAUSAL) {
     if (POS == POS_ANALYTIC) {
-      qpos = rvalid ? layout_pos(P.layout, P.N, P.blk, dev, la) : INT32_MIN;
-      qmin = layout_pos(P.layout, P.N, P.blk, dev, a0q);
-      qmax = layout_pos(P.layout, P.N, P.blk, dev, a0q + nrows - 1);
+      qpos = rvalid ? layout_pos(lay, P.N, P.blk, dev, la) : INT32_MIN;
+      qmin = layout_pos(lay, P.N, P.blk, dev, a0q);
+      qmax = layout_pos(lay, P.N, P.blk, dev, a0q + nrows - 1);
     } else {
       qpos = rvalid ? P.q_pos[qrow] : INT32_MIN;
       int mn = INT32_MAX, mx = INT32_MIN;
@@ -433,7 +446,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   [[maybe_unused]] unsigned dkn = 0, dvn = 0;
   [[maybe_unused]] int64_t cstep = 0;
   if constexpr (NAT) {
-    const int nstride = P.layout == RA_STRIPED ? P.N : 1;
+    const int nstride = lay == RA_STRIPED ? P.N : 1;
     const int row = wave * RPC + lane / UNITS;
     const int ph = lane % UNITS;
     dkn = (unsigned)(row * nstride * ROWB) + ((ph ^ (row & KMASK)) << 4);
@@ -480,20 +493,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     }
     const char* kb = reinterpret_cast<const char*>(Kg + T.start * D);
     const char* vb = reinterpret_cast<const char*>(Vg + T.start * D);
+    const int64_t rem = (P.Sk_tot - T.start) * ROWB;
+    const auto kr = rsrc(kb, rem), vr = rsrc(vb, rem);
     if (T.n == BN) {
 #pragma unroll
       for (int i = 0; i < XPW; ++i) {
         const int x = wave + NW * i;
-        // The copy's constant goes into the 32-bit lane offset, which the
-        // empty asm makes opaque: the address stays "scalar base + 32-bit
-        // offset" (global_load_lds with saddr).  Left to itself the compiler
-        // shares one 64-bit per-lane address between the copies and adds the
-        // constants in 64-bit VALU arithmetic, and the 64-bit-address form of
-        // the copy stalls the MFMAs around it.
-        unsigned ko = dk0 + i * NW * 1024, vo = dv0 + i * NW * 1024;
-        asm volatile("" : "+v"(ko), "+v"(vo));
-        dma16(kb + ko, kdst + x * 1024);
-        dma16(vb + vo, vdst + x * 1024);
+        bdma16(kr, dk0, (unsigned)(i * NW * 1024), kdst + x * 1024);
+        bdma16(vr, dv0, (unsigned)(i * NW * 1024), vdst + x * 1024);
       }
     } else {
 #pragma unroll
@@ -503,14 +510,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
         const int ph = lane % UNITS;
         const int rb = min(row, T.n - 1) * ROWB;
         unsigned ko = rb + ((ph ^ (row & KMASK)) << 4), vo = rb + ((ph ^ vswz(row)) << 4);
-        asm volatile("" : "+v"(ko), "+v"(vo));
-        dma16(kb + ko, kdst + x * 1024);
-        dma16(vb + vo, vdst + x * 1024);
+        bdma16(kr, ko, 0u, kdst + x * 1024);
+        bdma16(vr, vo, 0u, vdst + x * 1024);
       }
     }
   };
 
-  TileWalker<CAUSAL, POS, NAT> walker;
+  TileWalker<CAUSAL, POS, NAT, LAY> walker;
   walker.init(P);
   Tile cur;
   bool have = walker.next(P, dev, qmin, qmax, cur);
@@ -577,12 +583,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     return R;
   };
   // Part 2: exponentials of elements [e0, e1) of the half into pv, summed into ps.
-  auto softmax_exp = [&](const f32x16& sa, float msub, float* pv, float& ps, int e0, int e1) {
+  auto softmax_exp = [&](const f32x16& sa, float msub, float* pv, float& ps, float& psb, int e0,
+                         int e1) {
 #pragma unroll
-    for (int e = e0; e < e1; ++e) {
+    for (int e = e0; e < e1; ++e)
       pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], P.sl2, -msub));
-      ps += pv[e];
-    }
+#pragma unroll
+    for (int e = e0; e < e1; ++e) (e & 1 ? psb : ps) += pv[e];
   };
   auto pack_half = [&](const float* pv, u32x4& pf0, u32x4& pf1) {
     pf0 = u32x4{pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7])};
@@ -680,7 +687,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     u32x4 pf[2][2];
     Ref R0, R1;
     float pv0[16], pv1[16];
-    float ps0 = 0.f, ps1 = 0.f;
+    float ps0 = 0.f, ps1 = 0.f, ps0b = 0.f, ps1b = 0.f;
     u32x4 opd[PD + 1];
     static_for<PD>([&](auto I) __attribute__((always_inline)) {
       constexpr int st = decltype(I)::value;
@@ -703,7 +710,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
           if constexpr (STATE_IO) R0 = softmax_max(s0);
         }
         if constexpr (c >= 1)
-          softmax_exp(s0, STATE_IO ? R0.msub : msub, pv0, ps0, 16 * (c - 1) / (NC - 1),
+          softmax_exp(s0, STATE_IO ? R0.msub : msub, pv0, ps0, ps0b, 16 * (c - 1) / (NC - 1),
                       16 * c / (NC - 1));
       } else if constexpr (st < 2 * NC + NSTEP) {
         constexpr int v = st - 2 * NC, hh = v / NDB, db = v % NDB;
@@ -712,7 +719,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
           if constexpr (STATE_IO) R1 = softmax_max(s1);
         }
         if constexpr (v >= 1)
-          softmax_exp(s1, STATE_IO ? R1.msub : msub, pv1, ps1, 16 * (v - 1) / (NSTEP - 1),
+          softmax_exp(s1, STATE_IO ? R1.msub : msub, pv1, ps1, ps1b, 16 * (v - 1) / (NSTEP - 1),
                       16 * v / (NSTEP - 1));
       } else {
         constexpr int v = st - 2 * NC - NSTEP, hh = v / NDB, db = v % NDB;
@@ -724,9 +731,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       } else if constexpr (st == 2 * NC - 1) {
         if constexpr (STATE_IO) {
           pack_half(pv0, pf[0][0], pf[0][1]);
+          ps0 += ps0b;
           pin(pf[0][0], pf[0][1], ps0);
           softmax_close(R0, ps0);
         } else {
+          ps0 += ps0b;
           softmax_check(s0, pv0, ps0);
           pack_half(pv0, pf[0][0], pf[0][1]);
         }
@@ -734,9 +743,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       } else if constexpr (st == 2 * NC + NSTEP - 1) {
         if constexpr (STATE_IO) {
           pack_half(pv1, pf[1][0], pf[1][1]);
+          ps1 += ps1b;
           pin(pf[1][0], pf[1][1], ps1);
           softmax_close(R1, ps1);
         } else {
+          ps1 += ps1b;
           softmax_check(s1, pv1, ps1);
           pack_half(pv1, pf[1][0], pf[1][1]);
         }
@@ -835,7 +846,13 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
   hipError_t e;
   if (natural) {  // whole ring read and written in natural token order
     if (state_io || pos_mode == POS_ARRAY) return hipErrorInvalidValue;
-    if (causal)
+    if (causal && p.layout == RA_STRIPED)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, true, RA_STRIPED>),
+                         grid, block, 0, s, p, X);
+    else if (causal && p.layout == RA_ZIGZAG)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, true, RA_ZIGZAG>),
+                         grid, block, 0, s, p, X);
+    else if (causal)
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, true>), grid, block,
                          0, s, p, X);
     else
@@ -859,9 +876,15 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
     if (state_io)
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, true>), grid, block, 0, s,
                          p, X);
+    else if (p.layout == RA_CONTIGUOUS)  // ring launches: the layout fixed at compile time
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, false, RA_CONTIGUOUS>),
+                         grid, block, 0, s, p, X);
+    else if (p.layout == RA_STRIPED)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, false, RA_STRIPED>),
+                         grid, block, 0, s, p, X);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false>), grid, block, 0, s,
-                         p, X);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, false, RA_ZIGZAG>),
+                         grid, block, 0, s, p, X);
   }
   e = hipGetLastError();
   if (e == hipSuccess) xcd_after_launch(X, s);
