@@ -105,11 +105,13 @@ struct WsLayout {
 };
 
 // The matrix-core kernels read and write a whole striped / zigzag ring in
-// natural token order (rows addressed through the layout map); the vector
-// kernels run on device-ordered copies in the workspace.
+// natural token order (rows addressed through the layout map, 32-bit byte
+// offsets from the start of a key/value head, so heads under 4 GiB); the
+// vector kernels, and larger heads, run on device-ordered copies in the
+// workspace.
 bool ring_natural(const ra_dims* d, int layout, int device) {
   return device < 0 && layout != RA_CONTIGUOUS && d->dtype == RA_BF16 &&
-         ra::mfma_supports((int)d->D);
+         ra::mfma_supports((int)d->D) && d->Sk * d->D * elem_size(d->dtype) < (1LL << 32);
 }
 
 WsLayout ring_ws(const ra_dims* d, int layout, int device) {

@@ -28,9 +28,10 @@
 // ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element
 // i%4 of the 8 bytes that lane 4e + i/4 addressed, as its element e.
 //
-// Tiles move HBM -> LDS without registers (global_load_lds, 16 bytes per
-// lane), double-buffered, one barrier per tile; the next tile's copy is in
-// flight while the current one is computed.  Both tiles are row-major with
+// Tiles move HBM -> LDS without registers (buffer_load ... lds, 16 bytes per
+// lane, through a descriptor bounded by the key/value head), double-buffered,
+// one barrier per tile; the next tile's copy is in flight while the current
+// one is computed.  Both tiles are row-major with
 // the 16-byte units of a row XOR-swizzled (K by row, V by 4*(row bits)) so the MFMA
 // operand reads are free of bank conflicts; the swizzle is applied by choosing
 // which global unit each lane copies.
@@ -98,11 +99,6 @@ __device__ inline u32x4 lds_read128(const lds_t* p) {
 __device__ inline u32x2 lds_read_tr(const lds_t* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
   return __builtin_bit_cast(u32x2, v);
-}
-
-// 16 bytes per lane, global -> LDS at dst + 16*lane (dst uniform).
-__device__ inline void dma16(const void* src, lds_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -461,18 +457,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       // for device-ordered rows; only the source rows differ.
       const char* kn = reinterpret_cast<const char*>(Kg);
       const char* vn = reinterpret_cast<const char*>(Vg);
+      const int64_t head = P.Sk_tot * ROWB;
       if (T.n == BN && T.split >= BN) {
-        const char* kb = kn + (int64_t)T.p0 * ROWB;
-        const char* vb = vn + (int64_t)T.p0 * ROWB;
+        const int64_t t0 = (int64_t)T.p0 * ROWB;
+        const auto kr = rsrc(kn + t0, head - t0), vr = rsrc(vn + t0, head - t0);
 #pragma unroll
         for (int i = 0; i < XPW; ++i) {
           const int x = wave + NW * i;
-          unsigned ko = dkn, vo = dvn;
-          asm volatile("" : "+v"(ko), "+v"(vo));
-          dma16(kb + i * cstep + ko, kdst + x * 1024);
-          dma16(vb + i * cstep + vo, vdst + x * 1024);
+          bdma16(kr, dkn, (unsigned)(i * cstep), kdst + x * 1024);
+          bdma16(vr, dvn, (unsigned)(i * cstep), vdst + x * 1024);
         }
       } else {
+        const auto kr = rsrc(kn, head), vr = rsrc(vn, head);
         const int p0 = T.p0, p1 = T.p1, split = T.split, stride = T.stride, last = T.n - 1;
 #pragma unroll
         for (int i = 0; i < XPW; ++i) {
@@ -484,9 +480,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
           const int64_t tok = (int64_t)first + (int64_t)rr * stride;
           unsigned ko = (unsigned)(tok * ROWB) + ((ph ^ (row & KMASK)) << 4);
           unsigned vo = (unsigned)(tok * ROWB) + ((ph ^ vswz(row)) << 4);
-          asm volatile("" : "+v"(ko), "+v"(vo));
-          dma16(kn + ko, kdst + x * 1024);
-          dma16(vn + vo, vdst + x * 1024);
+          bdma16(kr, ko, 0u, kdst + x * 1024);
+          bdma16(vr, vo, 0u, vdst + x * 1024);
         }
       }
       return;

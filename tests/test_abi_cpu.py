@@ -134,6 +134,12 @@ def test_workspace_bytes(lib):
     for D in (32, 64, 128):
         assert ws(dims(Hq=32, Hkv=8, Sq=65536, Sk=65536, D=D), 8, 1, -1) == 0
         assert ws(dims(Hq=32, Hkv=8, Sq=65536, Sk=65536, D=D), 8, 2, -1) == 0
+    # ... as long as a key/value head stays under 4 GiB (32-bit offsets from the
+    # head's start); a larger one is permuted into the workspace
+    S = 1 << 24  # 2^24 tokens x 128 x 2 bytes = 4 GiB per head
+    assert ws(dims(Hq=1, Hkv=1, Sq=S - 16, Sk=S - 16), 8, 1, -1) == 0
+    big = ws(dims(Hq=1, Hkv=1, Sq=S, Sk=S), 8, 1, -1)
+    assert big == 4 * (S * 128 * 2) + S * 4 and capi.last_error() == ""
     # the vector kernels (fp32, or bf16 with D 8 / 16) work on device-ordered
     # copies: Q + out copies, K + V copies, lse copy
     for dtype, D, es in ((0, 128, 4), (1, 16, 2), (1, 8, 2)):
