@@ -109,6 +109,12 @@ __device__ inline void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
                                            voff, soff, 0, 0);
 }
+// The FLAT form, global -> LDS at dst + 16*lane (dst uniform), for kernels
+// whose scalar registers are too tight for two buffer descriptors.
+__device__ inline void dma16(const void* src, lds_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
 __device__ inline void wait_dma() {
   // vmcnt(0); expcnt and lgkmcnt left at their maxima (no wait)
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -449,6 +455,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     dvn = (unsigned)(row * nstride * ROWB) + ((ph ^ vswz(row)) << 4);
     cstep = (int64_t)NW * RPC * nstride * ROWB;
   }
+  // One 16-byte-per-lane copy: base + soff is the tile's uniform source and
+  // voff the lane's offset.  The 4-wave head-dim-128 kernels have no scalar
+  // registers to spare for the two descriptors and use the FLAT form, with the
+  // lane offset kept opaque so the address stays "scalar base + 32-bit
+  // offset" (the 64-bit-address form of the copy stalls the MFMAs around it).
+  constexpr bool kBufCopy = !(D == 128 && NW == 4);
+  auto copy16 = [&](const char* base, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                    lds_t* dst) {
+    if constexpr (kBufCopy) {
+      bdma16(r, voff, soff, dst);
+    } else {
+      unsigned o = voff;
+      asm volatile("" : "+v"(o));
+      dma16(base + soff + o, dst);
+    }
+  };
   auto issue_tile = [&](const Tile& T, lds_t* kdst) {
     lds_t* vdst = kdst + TILE_BYTES;
     if constexpr (NAT) {
@@ -464,8 +486,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
 #pragma unroll
         for (int i = 0; i < XPW; ++i) {
           const int x = wave + NW * i;
-          bdma16(kr, dkn, (unsigned)(i * cstep), kdst + x * 1024);
-          bdma16(vr, dvn, (unsigned)(i * cstep), vdst + x * 1024);
+          copy16(kn + t0, kr, dkn, (unsigned)(i * cstep), kdst + x * 1024);
+          copy16(vn + t0, vr, dvn, (unsigned)(i * cstep), vdst + x * 1024);
         }
       } else {
         const auto kr = rsrc(kn, head), vr = rsrc(vn, head);
@@ -480,8 +502,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
           const int64_t tok = (int64_t)first + (int64_t)rr * stride;
           unsigned ko = (unsigned)(tok * ROWB) + ((ph ^ (row & KMASK)) << 4);
           unsigned vo = (unsigned)(tok * ROWB) + ((ph ^ vswz(row)) << 4);
-          bdma16(kr, ko, 0u, kdst + x * 1024);
-          bdma16(vr, vo, 0u, vdst + x * 1024);
+          copy16(kn, kr, ko, 0u, kdst + x * 1024);
+          copy16(vn, vr, vo, 0u, vdst + x * 1024);
         }
       }
       return;
@@ -494,8 +516,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
 #pragma unroll
       for (int i = 0; i < XPW; ++i) {
         const int x = wave + NW * i;
-        bdma16(kr, dk0, (unsigned)(i * NW * 1024), kdst + x * 1024);
-        bdma16(vr, dv0, (unsigned)(i * NW * 1024), vdst + x * 1024);
+        copy16(kb, kr, dk0, (unsigned)(i * NW * 1024), kdst + x * 1024);
+        copy16(vb, vr, dv0, (unsigned)(i * NW * 1024), vdst + x * 1024);
       }
     } else {
 #pragma unroll
@@ -505,8 +527,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
         const int ph = lane % UNITS;
         const int rb = min(row, T.n - 1) * ROWB;
         unsigned ko = rb + ((ph ^ (row & KMASK)) << 4), vo = rb + ((ph ^ vswz(row)) << 4);
-        bdma16(kr, ko, 0u, kdst + x * 1024);
-        bdma16(vr, vo, 0u, vdst + x * 1024);
+        copy16(kb, kr, ko, 0u, kdst + x * 1024);
+        copy16(vb, vr, vo, 0u, vdst + x * 1024);
       }
     }
   };
@@ -847,9 +869,8 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
     else if (causal && p.layout == RA_ZIGZAG)
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, true, RA_ZIGZAG>),
                          grid, block, 0, s, p, X);
-    else if (causal)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, true>), grid, block,
-                         0, s, p, X);
+    else if (causal)  // natural order is only for striped and zigzag rings
+      return hipErrorInvalidValue;
     else
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, false, true>), grid, block, 0,
                          s, p, X);
@@ -868,10 +889,9 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
     else
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, false>), grid, block, 0, s, p, X);
   } else {
-    if (state_io)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, true>), grid, block, 0, s,
-                         p, X);
-    else if (p.layout == RA_CONTIGUOUS)  // ring launches: the layout fixed at compile time
+    if (state_io)  // the state-in-HBM steps take explicit positions
+      return hipErrorInvalidValue;
+    if (p.layout == RA_CONTIGUOUS)  // ring launches: the layout fixed at compile time
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, false, RA_CONTIGUOUS>),
                          grid, block, 0, s, p, X);
     else if (p.layout == RA_STRIPED)
