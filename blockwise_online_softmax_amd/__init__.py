@@ -15,7 +15,7 @@ from .capi import (  # noqa: F401
     LAYOUT_IDS, State, load, last_error, ra_block_step, ra_finalize, ra_layout_position, ra_merge,
     ra_permute,
     ra_positions, ra_ring, ra_ring_workspace_bytes, ra_state_init, ra_state_merge, ra_version,
-    ra_vocab_ce, ra_vocab_ce_combine, ra_vocab_ce_grad, ra_vocab_ce_shard,
+    ra_vocab_ce, ra_vocab_ce_combine, ra_vocab_ce_grad, ra_vocab_ce_shard, ra_vocab_ce_static,
     ra_vocab_ce_workspace_bytes, ra_xcd_plan, ra_xcd_speeds,
     ring_attention,
 )

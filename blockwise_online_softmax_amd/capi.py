@@ -38,8 +38,8 @@ EXPORTED = ["ra_state_init", "ra_block_step", "ra_finalize", "ra_ring",
             "ra_ring_workspace_bytes", "ra_permute", "ra_positions", "ra_layout_position",
             "ra_state_merge",
             "ra_merge", "ra_vocab_ce_shard", "ra_vocab_ce_combine", "ra_vocab_ce_grad",
-            "ra_vocab_ce_workspace_bytes", "ra_vocab_ce", "ra_xcd_plan", "ra_xcd_speeds",
-            "ra_last_error", "ra_version"]
+            "ra_vocab_ce_workspace_bytes", "ra_vocab_ce", "ra_vocab_ce_static", "ra_xcd_plan",
+            "ra_xcd_speeds", "ra_last_error", "ra_version"]
 
 
 class RaDims(ctypes.Structure):
@@ -88,6 +88,7 @@ def load(path=None):
                                    vp]),
         "ra_vocab_ce_workspace_bytes": (sz, [i64, i32]),
         "ra_vocab_ce": (i32, [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "ra_vocab_ce_static": (i32, [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp]),
         "ra_xcd_plan": (i64, [dims_p, i32, i32, i32, i32, vp, vp]),
         "ra_xcd_speeds": (i32, [vp, vp, i32]),
         "ra_last_error": (ctypes.c_char_p, []),
@@ -388,6 +389,21 @@ def ra_vocab_ce(logits, target, t, loss, mean_loss, lse=None, ws=None, stream=No
     _check(load().ra_vocab_ce(_ptr(logits), _ptr(target), N, V, int(t), _dtype_id(logits),
                               _ptr(loss), _ptr(mean_loss), _ptr(lse), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "ra_vocab_ce")
+
+
+def ra_vocab_ce_static(logits, target, t, loss, mean_loss, lse=None, stream=None):
+    """ra_vocab_ce with the library's static per-GPU scratch (no workspace)."""
+    torch = _torch()
+    _require(logits, "logits")
+    _require(target, "target", torch.int64)
+    _require(loss, "loss", torch.float32)
+    _require(mean_loss, "mean_loss", torch.float32)
+    if lse is not None:
+        _require(lse, "lse", torch.float32)
+    N, V = logits.shape
+    _check(load().ra_vocab_ce_static(_ptr(logits), _ptr(target), N, V, int(t), _dtype_id(logits),
+                                     _ptr(loss), _ptr(mean_loss), _ptr(lse), _stream(stream)),
+           "ra_vocab_ce_static")
 
 
 def ra_version():

@@ -411,9 +411,13 @@ size_t ra_vocab_ce_workspace_bytes(int64_t N, int t) {
   return (size_t)ce_workspace(N, t).total;
 }
 
-ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int64_t V, int t,
-                      ra_dtype dtype, float* loss, float* mean_loss, float* lse, void* ws,
-                      size_t ws_bytes, void* stream) {
+namespace {
+
+// Validation shared by ra_vocab_ce and ra_vocab_ce_static (everything but the
+// workspace).
+ra_status check_vocab_ce(const void* logits, const int64_t* target, int64_t N, int64_t V, int t,
+                         ra_dtype dtype, const float* loss, const float* mean_loss,
+                         const float* lse) {
   if (t < 1 || t > kMaxShards) return fail(RA_ERR_SHAPE, "t must be in [1, %d]", kMaxShards);
   if (V < 1 || V % t != 0) return fail(RA_ERR_SHAPE, "V must be a positive multiple of t");
   ra_status s = check_ce_rows(logits, V, target, N, V / t, dtype);
@@ -422,6 +426,38 @@ ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int6
     return fail(RA_ERR_NULL, "loss and mean_loss must be non-NULL");
   if (!aligned(loss, 4) || !aligned(mean_loss, 4) || (lse != nullptr && !aligned(lse, 4)))
     return fail(RA_ERR_SHAPE, "loss / mean_loss / lse misaligned");
+  return RA_OK;
+}
+
+// The shard and combine launches of the whole cross-entropy, with the
+// statistics and partial sums in `base` laid out as ce_workspace(N, t) says.
+ra_status vocab_ce_launch(const void* logits, const int64_t* target, int64_t N, int64_t V, int t,
+                          ra_dtype dtype, float* loss, float* mean_loss, float* lse, char* base,
+                          const CeWorkspace& w, void* stream) {
+  float* st = reinterpret_cast<float*>(base + w.stats);
+  float* partial = reinterpret_cast<float*>(base + w.partial);
+  const int64_t V_loc = V / t;
+  float* m = st;
+  float* zs = st + (int64_t)t * N;
+  float* pr = st + 2 * (int64_t)t * N;
+  (void)hipGetLastError();
+  ra_status s = hip_status(ra::launch_ce_stats(logits, V, target, N, V_loc, 0, t, dtype, m, zs,
+                                               pr, (hipStream_t)stream),
+                           "ra_vocab_ce shard launch");
+  if (s != RA_OK) return s;
+  s = hip_status(ra::launch_ce_combine(m, zs, pr, t, N, loss, lse, partial, mean_loss,
+                                       (hipStream_t)stream),
+                 "ra_vocab_ce combine launch");
+  return s == RA_OK ? ok() : s;
+}
+
+}  // namespace
+
+ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int64_t V, int t,
+                      ra_dtype dtype, float* loss, float* mean_loss, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  ra_status s = check_vocab_ce(logits, target, N, V, t, dtype, loss, mean_loss, lse);
+  if (s != RA_OK) return s;
   const CeWorkspace w = ce_workspace(N, t);
   if (ws == nullptr) return fail(RA_ERR_WORKSPACE, "workspace required (%lld bytes)", (long long)w.total);
   if ((int64_t)ws_bytes < w.total)
@@ -434,22 +470,32 @@ ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int6
     if (!aliasing_ok(outs, 3, ins, 3))
       return fail(RA_ERR_SHAPE, "loss / mean_loss / lse overlap each other, an input or the workspace");
   }
-  char* base = static_cast<char*>(ws);
-  float* st = reinterpret_cast<float*>(base + w.stats);
-  float* partial = reinterpret_cast<float*>(base + w.partial);
-  const int64_t V_loc = V / t;
-  float* m = st;
-  float* zs = st + (int64_t)t * N;
-  float* pr = st + 2 * (int64_t)t * N;
-  (void)hipGetLastError();
-  s = hip_status(ra::launch_ce_stats(logits, V, target, N, V_loc, 0, t, dtype, m, zs, pr,
-                                     (hipStream_t)stream),
-                 "ra_vocab_ce shard launch");
+  return vocab_ce_launch(logits, target, N, V, t, dtype, loss, mean_loss, lse,
+                         static_cast<char*>(ws), w, stream);
+}
+
+ra_status ra_vocab_ce_static(const void* logits, const int64_t* target, int64_t N, int64_t V,
+                             int t, ra_dtype dtype, float* loss, float* mean_loss, float* lse,
+                             void* stream) {
+  ra_status s = check_vocab_ce(logits, target, N, V, t, dtype, loss, mean_loss, lse);
   if (s != RA_OK) return s;
-  s = hip_status(ra::launch_ce_combine(m, zs, pr, t, N, loss, lse, partial, mean_loss,
-                                       (hipStream_t)stream),
-                 "ra_vocab_ce combine launch");
-  return s == RA_OK ? ok() : s;
+  const CeWorkspace w = ce_workspace(N, t);
+  if (w.total > ra::kCeStaticBytes)
+    return fail(RA_ERR_WORKSPACE,
+                "N = %lld rows over t = %d shards need %lld bytes of scratch, more than the "
+                "%lld-byte static scratch (ra_vocab_ce with a workspace has no such limit)",
+                (long long)N, t, (long long)w.total, (long long)ra::kCeStaticBytes);
+  {
+    const int64_t es = dtype == RA_BF16 ? 2 : 4;
+    const span ins[2] = {{logits, N * V * es, -1}, {target, N * 8, -2}};
+    const span outs[3] = {{loss, N * 4, 1}, {mean_loss, 4, 2}, {lse, lse != nullptr ? N * 4 : 0, 3}};
+    if (!aliasing_ok(outs, 3, ins, 2))
+      return fail(RA_ERR_SHAPE, "loss / mean_loss / lse overlap each other or an input");
+  }
+  char* base = static_cast<char*>(ra::ce_static_scratch());
+  if (base == nullptr)
+    return fail(RA_ERR_HIP, "no current HIP device, or the static scratch has no device address");
+  return vocab_ce_launch(logits, target, N, V, t, dtype, loss, mean_loss, lse, base, w, stream);
 }
 
 size_t ra_ring_workspace_bytes(const ra_dims* d, int N, ra_layout layout, int device) {

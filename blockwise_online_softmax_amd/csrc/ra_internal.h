@@ -182,6 +182,11 @@ hipError_t launch_ce_stats(const void* logits, int64_t ld, const int64_t* target
 int64_t ce_partial_count(int64_t N);
 hipError_t launch_ce_combine(const float* m, const float* s, const float* p, int t, int64_t N,
                              float* loss, float* lse, float* partial, float* mean, hipStream_t st);
+// ra_vocab_ce_static: bytes of its per-GPU scratch array, and the array's
+// device address on the current device (looked up on the first call on each
+// device; nullptr without a device or when the lookup fails).
+constexpr int64_t kCeStaticBytes = (int64_t)8 << 20;
+void* ce_static_scratch();
 hipError_t launch_ce_grad(const void* logits, int64_t ld, const int64_t* target, const float* lse,
                           int64_t N, int64_t V_loc, int64_t start0, int t, float scale, int dtype,
                           void* grad, int64_t ldg, hipStream_t st);

@@ -17,6 +17,8 @@
 // when the max rises and adds the exponentials (base 2, log2(e) folded into
 // one FMA).  Rows whose shard does not start on a 16-byte boundary take their
 // first and last few logits one at a time.
+#include <mutex>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -322,6 +324,38 @@ hipError_t launch_ce_grad(const void* logits, int64_t ld, const int64_t* target,
                          V_loc, start0, scale, grad, ldg, chunks);
   }
   return hipGetLastError();
+}
+
+// Scratch of ra_vocab_ce_static (for callers that cannot allocate): the
+// per-shard statistics and the partial sums of the mean, kCeStaticBytes on each
+// GPU the library runs on, held until the process ends.  In host code the name
+// `scratch` stands for a host-side shadow, not for the GPU's copy: the kernels
+// get the device address that hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ __align__(256) char scratch[kCeStaticBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device (nullptr: not looked up)
+}  // namespace
+
+void* ce_static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
 }
 
 }  // namespace ra

@@ -297,6 +297,24 @@ ra_status ra_vocab_ce(const void* logits, const int64_t* target, int64_t N, int6
                       ra_dtype dtype, float* loss, float* mean_loss, float* lse, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* ra_vocab_ce without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  It computes exactly what ra_vocab_ce computes, with
+ * the same kernels, but keeps the shard statistics and partial sums in a
+ * static array of the library: 8 MiB (8388608 bytes) on each GPU it runs on,
+ * reserved when the library is loaded and held until the process ends; this
+ * call allocates nothing.  Sizes whose scratch, ra_vocab_ce_workspace_bytes(N,
+ * t), exceeds 8 MiB are rejected with RA_ERR_WORKSPACE (for t = 8 shards, N up
+ * to about 87,000 rows).  Every call on one GPU shares that GPU's array, and
+ * the array keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from several threads without ordering) race, so order
+ * them on one stream.  The stream must belong to the current device.  Other
+ * arguments and errors as for ra_vocab_ce; RA_ERR_HIP without a current
+ * device. */
+ra_status ra_vocab_ce_static(const void* logits, const int64_t* target, int64_t N, int64_t V,
+                             int t, ra_dtype dtype, float* loss, float* mean_loss, float* lse,
+                             void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);
 

@@ -224,6 +224,26 @@ def test_vocab_ce_errors(lib):
     expect(G(L, 16, T, lse, 4, 16, 0, 1.0, 1, lse - 16, 16, None), capi.RA_ERR_SHAPE, "overlap")
 
 
+def test_vocab_ce_static_errors(lib):
+    """ra_vocab_ce_static validates like ra_vocab_ce and rejects sizes whose
+    scratch exceeds its 8 MiB static array, all before any HIP call."""
+    V = lib.ra_vocab_ce_static
+    L, T = FAKE, FAKE + (1 << 30)
+    loss, mean = FAKE + (2 << 30), FAKE + (3 << 30)
+    W = lib.ra_vocab_ce_workspace_bytes
+    assert W(87000, 8) <= 8 << 20 < W(100000, 8)
+    expect(V(L, T, 100000, 16, 8, 1, loss, mean, None, None), capi.RA_ERR_WORKSPACE,
+           "static scratch")
+    expect(V(L, T, 4, 15, 2, 1, loss, mean, None, None), capi.RA_ERR_SHAPE, "multiple")
+    expect(V(L, T, 4, 16, 0, 1, loss, mean, None, None), capi.RA_ERR_SHAPE, "t must")
+    expect(V(None, T, 4, 16, 2, 1, loss, mean, None, None), capi.RA_ERR_NULL, "logits")
+    expect(V(L, T, 4, 16, 2, 1, loss, None, None, None), capi.RA_ERR_NULL, "mean_loss")
+    expect(V(L, T, 4, 16, 2, 1, L + 32, mean, None, None), capi.RA_ERR_SHAPE, "overlap")
+    expect(V(L, T, 4, 16, 2, 1, loss, loss + 8, None, None), capi.RA_ERR_SHAPE, "overlap")
+    if torch.cuda.device_count() == 0:  # valid arguments, but no device to run on
+        expect(V(L, T, 4, 16, 2, 1, loss, mean, None, None), capi.RA_ERR_HIP, "device")
+
+
 def test_layout_position_matches_oracle(lib):
     """The layout map the kernels use (compiled for the host through the ABI)
     against the oracle's maps, for every layout, whole sequences and device
