@@ -53,7 +53,17 @@
 extern "C" {
 #endif
 
-typedef enum ra_status {
+/* The enums are int-sized.  Compiled as C++ they get int32_t as their fixed
+ * underlying type: a C caller may pass any int where an enum is expected, and
+ * the implementation validates it, which is only well defined in C++ when the
+ * enum can hold every int32_t value. */
+#ifdef __cplusplus
+#define RA_ENUM_BASE : int32_t
+#else
+#define RA_ENUM_BASE
+#endif
+
+typedef enum ra_status RA_ENUM_BASE {
   RA_OK = 0,
   RA_ERR_NULL = 1,        /* a required pointer is NULL                      */
   RA_ERR_SHAPE = 2,       /* sizes inconsistent, not divisible, misaligned   */
@@ -64,8 +74,8 @@ typedef enum ra_status {
   RA_ERR_HIP = 7          /* the HIP runtime reported an error on launch     */
 } ra_status;
 
-typedef enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
-typedef enum ra_mask { RA_MASK_NONE = 0, RA_MASK_CAUSAL = 1 } ra_mask;
+typedef enum ra_dtype RA_ENUM_BASE { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+typedef enum ra_mask RA_ENUM_BASE { RA_MASK_NONE = 0, RA_MASK_CAUSAL = 1 } ra_mask;
 
 /* Token -> device layouts of a sequence of S tokens over N devices
  * (blk = S/N tokens each; local index a = 0..blk-1, ascending positions):
@@ -76,7 +86,7 @@ typedef enum ra_mask { RA_MASK_NONE = 0, RA_MASK_CAUSAL = 1 } ra_mask;
  *                                 a >= c: pos = (2N-1-p)*c + (a-c)
  *                  (needs S % 2N == 0).
  * "Device order" concatenates the N device blocks, device 0 first. */
-typedef enum ra_layout { RA_CONTIGUOUS = 0, RA_STRIPED = 1, RA_ZIGZAG = 2 } ra_layout;
+typedef enum ra_layout RA_ENUM_BASE { RA_CONTIGUOUS = 0, RA_STRIPED = 1, RA_ZIGZAG = 2 } ra_layout;
 
 typedef struct ra_dims {
   int64_t B, Hq, Hkv; /* batch, query heads, key/value heads (Hq % Hkv == 0) */
