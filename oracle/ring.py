@@ -4,13 +4,10 @@ TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
 Recurrence: [M23] "The Math: One Block at a Time".  Each query row keeps a
 running max m, a running denominator l and an unnormalised output o.  When a
-key/value block with scores s_ij = q_i . k_j / sqrt(d) arrives:
-    m_new = max(m, max_j s_ij)
-    c     = exp(m - m_new)                 (rescales what is already summed)
-    l     = l * c + sum_j exp(s_ij - m_new)
-    o     = o * c + sum_j exp(s_ij - m_new) v_j
-    m     = m_new
-and at the end out = o / l.  [RAQA] "The ring" runs the same loop in numpy
+key/value block with scores s_ij = q_i . k_j / sqrt(d) arrives, the new
+running max is the larger of m and the block's largest score; what is already
+summed is rescaled by exp(m_old - m_new); the block adds exp(s_ij - m_new) to l
+and exp(s_ij - m_new) v_j to o.  At the end out = o / l.  [RAQA] "The ring" runs the same loop in numpy
 with m = -inf, l = 0, o = 0 as the start; [DT2] "Ring Attention" starts m at
 -1e30 instead.  Reading taken: start at -inf and guard the case where no key
 has been visible yet (m_new = -inf): then c = 1 and the block adds nothing,
@@ -46,20 +43,31 @@ def absorb_block(state, q, k, v, scale, visible=None):
     """Fold one key/value block into the running state; returns the new state.
 
     q [r, D]; k, v [n, D]; visible [r, n] bool (None: all pairs visible).
+
+    The block is reduced on its own first: m_b, its row max over the visible
+    scores; l_b, the sum of exp(s - m_b); o_b, the sum of exp(s - m_b) v.
+    Folding it in is then the recurrence's update written with the block's
+    own sums: the running max becomes max(m, m_b), and the old sums and the
+    block's are each brought to it (factors exp(m - m') and exp(m_b - m'))
+    before they are added.  A block with no visible key for a row adds
+    nothing to it; a row that has seen nothing keeps m = -inf, l = 0, o = 0.
     """
     m, l, o = state
     s = (q @ k.T) * scale
     if visible is not None:
         s = np.where(visible, s, -np.inf)
-    m_new = np.maximum(m, s.max(axis=1))
-    seen = np.isfinite(m_new)
-    m_ref = np.where(seen, m_new, 0.0)
-    c = np.where(seen, np.exp(m - m_ref), 1.0)
-    p = np.exp(s - m_ref[:, None])  # masked entries: exp(-inf) = 0
-    p = np.where(seen[:, None], p, 0.0)
-    l = l * c + p.sum(axis=1)
-    o = o * c[:, None] + p @ v
-    return (m_new, l, o)
+    # the block on its own
+    m_b = s.max(axis=1)
+    has = np.isfinite(m_b)  # rows that see a key of this block
+    e = np.exp(s - np.where(has, m_b, 0.0)[:, None])  # 0 on masked entries
+    l_b = np.where(has, e.sum(axis=1), 0.0)
+    o_b = np.where(has[:, None], e @ v, 0.0)
+    # both sides at the new running max
+    m_new = np.maximum(m, m_b)
+    ref = np.where(np.isfinite(m_new), m_new, 0.0)
+    w_old = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
+    w_blk = np.where(has, np.exp(m_b - ref), 0.0)
+    return (m_new, l * w_old + l_b * w_blk, o * w_old[:, None] + o_b * w_blk[:, None])
 
 
 def finalize(state):

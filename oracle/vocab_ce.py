@@ -8,12 +8,11 @@ Definition ([DT2] "Vocab-parallel cross-entropy"): for logits z of shape
     loss_r = logsumexp(z_r) - z_r[t_r]
 and the reported loss is the mean over rows.  The page computes it with the
 vocab split into `t` contiguous shards of V_loc = V / t columns (rank k owns
-columns [k V_loc, (k+1) V_loc)), in three steps:
-    1. m   = max over shards of the shard's row max          (all-reduce MAX)
-    2. Z   = sum over shards of sum_j exp(z_kj - m)           (all-reduce SUM)
-    3. z_t = sum over shards of the shard's target logit, where a shard that
-             does not own t_r contributes 0                   (all-reduce SUM)
-    loss = log Z + m - z_t.
+columns [k V_loc, (k+1) V_loc)): the global row max, the sum of the shards'
+exponentials against it, and the target logit (contributed by the shard that
+owns it, 0 elsewhere), each reduced across ranks; the loss is log Z + max -
+target logit.  Here the shards' (max, sum) pairs are merged in the log domain
+instead, which gives the same log Z.
 Its gradient with respect to the logits of the mean loss is
     (softmax(z_r) - onehot(t_r)) / N,
 already split along the vocab like the logits.
@@ -26,8 +25,8 @@ Readings taken (the page is silent on them):
 Functions:
   cross_entropy_rows(z, target)   plain definition, per row (scipy's
                                   logsumexp of the row minus the target logit)
-  vocab_parallel(z, target, t)    the page's three steps over t shards,
-                                  per-row loss, the mean, and m + log Z
+  vocab_parallel(z, target, t)    over t shards: per-shard statistics merged
+                                  by log-sum-exp; per-row loss, the mean, log Z
   shard_stats(z_shard, target, start)
                                   one shard's (row max, sum of exp(z - that
                                   max), owned target logit)
@@ -56,41 +55,42 @@ def cross_entropy_rows(z, target):
 
 
 def shard_stats(z_shard, target, start):
-    """One shard's row max, sum of exp(z - row max) and owned target logit."""
+    """One shard's row max, sum of exp(z - row max) and owned target logit.
+    A row whose logits are all -inf has max -inf and sum 0 (a +inf or NaN
+    logit leaves the sum NaN)."""
     z = _as_f64(z_shard)
     t = _targets(target)
     V_loc = z.shape[1]
     m = z.max(axis=1)
-    s = np.exp(z - m[:, None]).sum(axis=1)
+    s = np.exp(z - np.where(m == -np.inf, 0.0, m)[:, None]).sum(axis=1)
     own = (t >= start) & (t < start + V_loc)
     pred = np.where(own, z[np.arange(len(t)), np.clip(t - start, 0, V_loc - 1)], 0.0)
     return m, s, pred
 
 
 def vocab_parallel(z, target, t):
-    """The page's three steps over t contiguous vocab shards.
+    """The loss over t contiguous vocab shards, from per-shard statistics.
 
-    Returns (loss per row, mean loss, lse = m + log Z per row)."""
+    Each shard is reduced on its own (shard_stats).  Its log-normaliser,
+    log sum_j exp(z_j) over its columns, is m_k + log s_k; the log-normaliser
+    of a union of shards is the log-sum-exp of theirs (an associative merge,
+    so the order of the shards does not matter), and the target logit is the
+    sum of the owned ones (at most one shard owns a target).
+    Returns (loss per row, mean loss, lse = log Z per row)."""
     z = _as_f64(z)
     tg = _targets(target)
     N, V = z.shape
     assert V % t == 0, "the page splits the vocab evenly (V_loc = V / t)"
     V_loc = V // t
-    shards = [z[:, k * V_loc:(k + 1) * V_loc] for k in range(t)]
-    # 1) global row max (all-reduce MAX over the shards' row maxima)
-    m = np.max(np.stack([sh.max(axis=1) for sh in shards]), axis=0)
-    # 2) global normaliser (all-reduce SUM of each shard's exp-sum against m)
-    Z = np.sum(np.stack([np.exp(sh - m[:, None]).sum(axis=1) for sh in shards]), axis=0)
-    # 3) the target logit: only the owning shard contributes
-    preds = []
-    for k, sh in enumerate(shards):
-        start = k * V_loc
-        own = (tg >= start) & (tg < start + V_loc)
-        local = np.clip(tg - start, 0, V_loc - 1)
-        preds.append(np.where(own, sh[np.arange(N), local], 0.0))
-    pred = np.sum(np.stack(preds), axis=0)
-    loss = np.log(Z) + m - pred
-    return loss, float(loss.mean()), m + np.log(Z)
+    stats = [shard_stats(z[:, k * V_loc:(k + 1) * V_loc], tg, k * V_loc) for k in range(t)]
+    with np.errstate(divide="ignore"):  # log 0 = -inf for a shard of -inf logits
+        log_z = [m + np.log(s) for m, s, _ in stats]
+    lse = log_z[0]
+    for lz in log_z[1:]:
+        lse = np.logaddexp(lse, lz)
+    pred = np.sum(np.stack([p for _, _, p in stats]), axis=0)
+    loss = lse - pred
+    return loss, float(loss.mean()), lse
 
 
 def ce_grad(z, target, scale):

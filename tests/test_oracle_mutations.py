@@ -18,10 +18,13 @@ import oracle_pins
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
 MUTATIONS = [
-    ("ring.py", "o = o * c[:, None] + p @ v", "o = o + p @ v", "drop rescale of o"),
-    ("ring.py", "l = l * c + p.sum(axis=1)", "l = l + p.sum(axis=1)", "drop rescale of l"),
-    ("ring.py", "np.exp(m - m_ref)", "np.exp(m_ref - m)", "wrong sign of rescale"),
-    ("ring.py", "m_new = np.maximum(m, s.max(axis=1))", "m_new = s.max(axis=1)", "forget running max"),
+    ("ring.py", "o * w_old[:, None] + o_b", "o + o_b", "drop rescale of o"),
+    ("ring.py", "l * w_old + l_b * w_blk", "l + l_b * w_blk", "drop rescale of l"),
+    ("ring.py", "np.exp(m - ref)", "np.exp(ref - m)", "wrong sign of rescale"),
+    ("ring.py", "np.exp(m_b - ref)", "np.exp(ref - m_b)", "wrong sign of the block's weight"),
+    ("ring.py", "e = np.exp(s - np.where(has, m_b, 0.0)[:, None])", "e = np.exp(s)",
+     "block sums not taken against the block max"),
+    ("ring.py", "m_new = np.maximum(m, m_b)", "m_new = m_b", "forget running max"),
     ("ring.py", "[(p - s) % N for s", "[(p + s) % N for s", "rotation direction"),
     ("ring.py", "lse = np.where(pos, m + np.log(safe_l)", "lse = np.where(pos, m - np.log(safe_l)", "lse sign"),
     ("ring.py", "vis = (kp[None, :] <= qp[:, None])", "vis = (kp[None, :] < qp[:, None])", "ring mask excludes diagonal"),
@@ -53,11 +56,14 @@ MUTATIONS = [
     ("merge.py", "return np.where(finite, np.exp(np.where(finite, x, 0.0) - np.where(finite, ref, 0.0)), 0.0)",
      "return np.where(finite, np.exp(np.where(finite, x, 0.0) - np.where(finite, ref, 0.0)), 1.0)",
      "empty side weighted 1"),
-    ("vocab_ce.py", "loss = np.log(Z) + m - pred", "loss = np.log(Z) - pred", "vocab loss drops max"),
-    ("vocab_ce.py", "own = (tg >= start) & (tg < start + V_loc)\n        local",
-     "own = (tg >= start) & (tg <= start + V_loc)\n        local", "vocab shard owns next shard's first id"),
-    ("vocab_ce.py", "Z = np.sum(np.stack([np.exp(sh - m[:, None])", "Z = np.sum(np.stack([np.exp(sh)",
+    ("vocab_ce.py", "log_z = [m + np.log(s)", "log_z = [np.log(s)", "vocab log-normaliser drops max"),
+    ("vocab_ce.py", "own = (t >= start) & (t < start + V_loc)\n    pred",
+     "own = (t >= start) & (t <= start + V_loc)\n    pred", "vocab shard owns next shard's first id"),
+    ("vocab_ce.py", "s = np.exp(z - np.where(m == -np.inf, 0.0, m)[:, None])", "s = np.exp(z)",
      "vocab sum not shifted by max"),
+    ("vocab_ce.py", "lse = np.logaddexp(lse, lz)", "lse = np.maximum(lse, lz)",
+     "shards merged by max instead of log-sum-exp"),
+    ("vocab_ce.py", "loss = lse - pred", "loss = lse + pred", "vocab loss target sign"),
     ("vocab_ce.py", "g[np.arange(N)[own], tg[own]] -= 1.0", "g[np.arange(N)[own], tg[own]] += 1.0",
      "gradient one-hot sign"),
     ("vocab_ce.py", "    return g * scale", "    return g", "gradient scale dropped"),
