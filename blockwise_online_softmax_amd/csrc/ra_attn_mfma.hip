@@ -854,8 +854,7 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
   AttnParams p = p0;
   p.ntq = (p.qlen + NW * 32 - 1) / (NW * 32);
   const int64_t nwg = (int64_t)p.B * p.Hq * p.nqblk * p.ntq;
-  int rows, per_cu;
-  mfma_geometry(D, p.qlen, &rows, &per_cu);
+  const int rows = NW * 32, per_cu = NW == 8 ? 1 : 2;
   const bool ring = !state_io && pos_mode != POS_ARRAY;
   XcdPlan X;
   const int64_t ngrid = xcd_prepare(p, nwg, causal, ring, rows, per_cu, s, &X);
@@ -878,19 +877,26 @@ hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_
     if (e == hipSuccess) xcd_after_launch(X, s);
     return e;
   }
-  if (!causal) {
-    if (state_io)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, true>), grid, block, 0, s, p, X);
-    else
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, false>), grid, block, 0, s, p, X);
-  } else if (pos_mode == POS_ARRAY) {
-    if (state_io)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, true>), grid, block, 0, s, p, X);
-    else
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, false>), grid, block, 0, s, p, X);
-  } else {
-    if (state_io)  // the state-in-HBM steps take explicit positions
+  if (state_io) {
+    // the state-in-HBM steps run 4-wave workgroups only: two share a CU, so
+    // one's state loads and stores overlap the other's matrix work
+    if constexpr (NW == 8) {
       return hipErrorInvalidValue;
+    } else {
+      if (!causal)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, true>), grid, block, 0, s, p,
+                           X);
+      else if (pos_mode == POS_ARRAY)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, true>), grid, block, 0, s, p,
+                           X);
+      else  // the state-in-HBM steps take explicit positions
+        return hipErrorInvalidValue;
+    }
+  } else if (!causal) {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NW, false, POS_NONE, false>), grid, block, 0, s, p, X);
+  } else if (pos_mode == POS_ARRAY) {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ARRAY, false>), grid, block, 0, s, p, X);
+  } else {
     if (p.layout == RA_CONTIGUOUS)  // ring launches: the layout fixed at compile time
       hipLaunchKernelGGL((attn_mfma_kernel<D, NW, true, POS_ANALYTIC, false, false, RA_CONTIGUOUS>),
                          grid, block, 0, s, p, X);
@@ -930,9 +936,10 @@ hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mod
   switch (D) {
     case 32: return launch_d<32, 4>(p, causal, pos_mode, state_io, natural, s);
     case 64: return launch_d<64, 4>(p, causal, pos_mode, state_io, natural, s);
-    case 128:  // 8 waves (256 query rows) once a block has that many rows
-      return p.qlen >= 256 ? launch_d<128, 8>(p, causal, pos_mode, state_io, natural, s)
-                           : launch_d<128, 4>(p, causal, pos_mode, state_io, natural, s);
+    case 128:  // 8 waves (256 query rows) once a ring block has that many rows
+      return (p.qlen >= 256 && !state_io)
+                 ? launch_d<128, 8>(p, causal, pos_mode, state_io, natural, s)
+                 : launch_d<128, 4>(p, causal, pos_mode, state_io, natural, s);
     default: return hipErrorInvalidValue;
   }
 }

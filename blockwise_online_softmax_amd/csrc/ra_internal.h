@@ -131,7 +131,7 @@ hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mod
                             bool natural, hipStream_t s);
 bool mfma_supports(int D);
 // Rows per workgroup and resident workgroups per CU of the matrix-core kernel
-// for a query block of `qlen` rows.
+// in a ring launch (state kept on chip) over a query block of `qlen` rows.
 void mfma_geometry(int D, int qlen, int* rows, int* per_cu);
 // Device address, on the current device, of the XCD stamp array (nullptr on
 // failure).
