@@ -194,7 +194,9 @@ struct TileWalker {
     const int lay = LAY >= 0 ? LAY : P.layout;
     while (s < P.nkblk) {
       if (tt == 0) {
-        j = ((dev - s) % P.nkblk + P.nkblk) % P.nkblk;  // ring order
+        // ring order (uniform; the first-lane read keeps it scalar, as the
+        // remainder is computed in vector registers)
+        j = __builtin_amdgcn_readfirstlane(((dev - s) % P.nkblk + P.nkblk) % P.nkblk);
         bfull = !CAUSAL;
         if (CAUSAL && POS == POS_ANALYTIC) {
           const int kf = layout_pos(lay, P.N, P.blk, j, 0);
@@ -319,9 +321,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   item_tile(lay, CAUSAL && POS == POS_ANALYTIC, P.nqblk, P.ntq, NW * 32, P.blk,
             (int)(L % nt), qi, t);
   L /= nt;
-  const int g = (int)(L % P.Hkv);
-  const int b = (int)(L / P.Hkv);
-  const int h = g * G + hg;
+  // Integer division has no scalar form, so the decode above may leave its
+  // results in vector registers; they are uniform over the workgroup, and
+  // reading the first lane keeps every position and bound derived from them
+  // (the walker's included) in scalar registers.
+  const int g = __builtin_amdgcn_readfirstlane((int)(L % P.Hkv));
+  const int b = __builtin_amdgcn_readfirstlane((int)(L / P.Hkv));
+  qi = __builtin_amdgcn_readfirstlane(qi);
+  t = __builtin_amdgcn_readfirstlane(t);
+  const int h = g * G + __builtin_amdgcn_readfirstlane(hg);
   const int dev = P.dev0 + qi;
 
   const int a0q = t * (NW * 32);                // first local row of the tile
@@ -481,7 +489,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       const char* vn = reinterpret_cast<const char*>(Vg);
       const int64_t head = P.Sk_tot * ROWB;
       if (T.n == BN && T.split >= BN) {
-        const int64_t t0 = (int64_t)T.p0 * ROWB;
+        // The tile's fields are wave-uniform, but the compiler may hold them
+        // in vector registers (zigzag positions are a select between two
+        // chunk formulas); reading the first lane keeps the descriptor base
+        // scalar, so the copies need no per-lane descriptor loop.
+        const int64_t t0 = (int64_t)__builtin_amdgcn_readfirstlane(T.p0) * ROWB;
         const auto kr = rsrc(kn + t0, head - t0), vr = rsrc(vn + t0, head - t0);
 #pragma unroll
         for (int i = 0; i < XPW; ++i) {
