@@ -174,7 +174,9 @@ struct Tile {
 // LAY: the layout when fixed at compile time (RA_CONTIGUOUS, RA_STRIPED,
 // RA_ZIGZAG), or -1 to read it from the parameters.  A fixed layout turns the
 // walker's position arithmetic into a few scalar instructions per tile.
-template <bool CAUSAL, int POS, bool NAT, int LAY = -1>
+// FAST: take the straight-line path for tiles inside a wholly visible block
+// (off where the scalar registers cannot hold its extra state).
+template <bool CAUSAL, int POS, bool NAT, int LAY = -1, bool FAST = true>
 struct TileWalker {
   int s, tt, j;
   bool bfull;
@@ -188,10 +190,41 @@ struct TileWalker {
     ntile_blk = (P.klen + BN - 1) / BN;
   }
 
+  // Positions of the keys of the tile at local index a0 of block j (the
+  // layouts are piecewise linear in the local index).
+  __device__ void positions(const AttnParams& P, int lay, int a0, int n, Tile& T) const {
+    T.p0 = layout_pos(lay, P.N, P.blk, j, a0);
+    T.stride = lay == RA_STRIPED ? P.N : 1;
+    T.split = BN;
+    T.p1 = T.p0;
+    if (lay == RA_ZIGZAG) {
+      const int c = P.blk >> 1;
+      if (a0 < c && a0 + n > c) {
+        T.split = c - a0;
+        T.p1 = layout_pos(lay, P.N, P.blk, j, c) - (c - a0);
+      }
+    }
+  }
+
   // Advance to the next tile with at least one visible pair.
   __device__ bool next(const AttnParams& P, int dev, int qmin, int qmax, Tile& T) {
     const int lane = threadIdx.x & 63;
     const int lay = LAY >= 0 ? LAY : P.layout;
+    // The common case first, as straight-line code: the next tile inside a
+    // block whose keys are all visible (no mask, nothing to skip).
+    if (FAST && POS != POS_ARRAY && bfull && tt > 0 && tt < ntile_blk) {
+      const int a0 = tt * BN;
+      const int n = min(BN, P.klen - a0);
+      T.start = (int64_t)j * P.klen + a0;
+      T.n = n;
+      T.kp = 0;
+      T.full = n == BN;
+      // positions: for natural-order copies, and for the mask of a ragged
+      // last tile (its keys past n are masked through the general path)
+      if (NAT || (CAUSAL && POS == POS_ANALYTIC && n < BN)) positions(P, lay, a0, n, T);
+      ++tt;
+      return true;
+    }
     while (s < P.nkblk) {
       if (tt == 0) {
         // ring order (uniform; the first-lane read keeps it scalar, as the
@@ -219,23 +252,11 @@ struct TileWalker {
       T.n = n;
       T.kp = 0;
       bool full = (n == BN);
-      if (NAT && !(CAUSAL && POS == POS_ANALYTIC)) {
-        // natural-order rows: position of the tile's keys (no mask needed)
-        T.p0 = layout_pos(lay, P.N, P.blk, j, a0);
-        T.stride = lay == RA_STRIPED ? P.N : 1;
-        T.split = BN;
-        T.p1 = T.p0;
-        if (lay == RA_ZIGZAG) {
-          const int c = P.blk >> 1;
-          if (a0 < c && a0 + n > c) {
-            T.split = c - a0;
-            T.p1 = layout_pos(lay, P.N, P.blk, j, c) - (c - a0);
-          }
-        }
-      }
+      if (NAT && !(CAUSAL && POS == POS_ANALYTIC))
+        positions(P, lay, a0, n, T);  // natural-order rows (no mask needed)
       if (CAUSAL && POS == POS_ANALYTIC) {
-        const int kf = layout_pos(lay, P.N, P.blk, j, a0);
         if (!bfull) {
+          const int kf = layout_pos(lay, P.N, P.blk, j, a0);
           const int kl = layout_pos(lay, P.N, P.blk, j, a0 + n - 1);
           if (kf > qmax) {  // positions ascend in a block: nothing after is visible
             ++s;
@@ -244,17 +265,7 @@ struct TileWalker {
           }
           full = full && (kl <= qmin);
         }
-        T.stride = lay == RA_STRIPED ? P.N : 1;
-        T.p0 = kf;
-        T.split = BN;
-        T.p1 = kf;
-        if (lay == RA_ZIGZAG) {
-          const int c = P.blk >> 1;
-          if (a0 < c && a0 + n > c) {
-            T.split = c - a0;
-            T.p1 = layout_pos(lay, P.N, P.blk, j, c) - (c - a0);
-          }
-        }
+        positions(P, lay, a0, n, T);
       }
       ++tt;
       if (CAUSAL && POS == POS_ARRAY) {
@@ -545,7 +556,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     }
   };
 
-  TileWalker<CAUSAL, POS, NAT, LAY> walker;
+  // (the zigzag kernels run out of scalar registers with the fast path)
+  TileWalker<CAUSAL, POS, NAT, LAY, LAY != RA_ZIGZAG> walker;
   walker.init(P);
   Tile cur;
   bool have = walker.next(P, dev, qmin, qmax, cur);
@@ -553,7 +565,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   wait_dma();
   __syncthreads();
 
-  // Causal / ragged mask of one 32-key half (partial tiles only).
+  // Causal / ragged mask of one 32-key half (partial tiles only).  The rare
+  // branches of the tile (mask, redo, rescale) are marked unlikely, so their
+  // code is laid out away from the straight-line path.
   auto mask_half = [&](f32x16& sa, int kb, const Tile& T) {
     if (CAUSAL && POS == POS_ANALYTIC && T.n == BN && T.split >= BN) {
       // Full tile with one linear position map (the common case): key kt is
@@ -629,7 +643,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   // raised a reference (rare under the lazy rule, so the factor and the
   // multiplications sit behind a wave-uniform branch), then add the sum.
   auto softmax_close = [&](const Ref& R, float ps) {
-    if (R.any) {
+    if (__builtin_expect(R.any, 0)) {
       // 1 where this lane kept its reference (also when both are -inf)
       const float alpha = R.mold == m2 ? 1.0f : __builtin_amdgcn_exp2f(R.mold - m2);
       lsum *= alpha;
@@ -645,7 +659,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   // the wave takes the pair max, raises m2 where it is exceeded, redoes the
   // half's exponentials and rescales l and o; then the sum joins l.
   auto softmax_check = [&](const f32x16& sa, float* pv, float& ps) {
-    if (__any(!(ps <= plim))) {
+    if (__builtin_expect(__any(!(ps <= plim)), 0)) {
       float tmax = sa[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sa[i]);
@@ -756,7 +770,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (st == NC - 1) {
-        if (!ct.full) mask_half(s0, 0, ct);
+        if (__builtin_expect(!ct.full, 0)) mask_half(s0, 0, ct);
       } else if constexpr (st == 2 * NC - 1) {
         if constexpr (STATE_IO) {
           pack_half(pv0, pf[0][0], pf[0][1]);
@@ -768,7 +782,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
           softmax_check(s0, pv0, ps0);
           pack_half(pv0, pf[0][0], pf[0][1]);
         }
-        if (!ct.full) mask_half(s1, 1, ct);
+        if (__builtin_expect(!ct.full, 0)) mask_half(s1, 1, ct);
       } else if constexpr (st == 2 * NC + NSTEP - 1) {
         if constexpr (STATE_IO) {
           pack_half(pv1, pf[1][0], pf[1][1]);
