@@ -174,19 +174,26 @@ struct Tile {
 // LAY: the layout when fixed at compile time (RA_CONTIGUOUS, RA_STRIPED,
 // RA_ZIGZAG), or -1 to read it from the parameters.  A fixed layout turns the
 // walker's position arithmetic into a few scalar instructions per tile.
-// FAST: take the straight-line path for tiles inside a wholly visible block
-// (off where the scalar registers cannot hold its extra state).
-template <bool CAUSAL, int POS, bool NAT, int LAY = -1, bool FAST = true>
+// Walks the key tiles of one query tile in ring order.  With analytic
+// positions, the tiles of a key block that the query tile sees, and among
+// them the ones it sees whole, are found once per block: positions ascend
+// inside a block, so both sets are prefixes of the block's tiles, bounded by
+// a binary search (tend: first tile whose first key is past the query tile's
+// last position; tfull: first tile whose last key is past its first).  Every
+// tile is then a few scalar instructions.  With position arrays, each tile is
+// classified from the min / max of its keys' positions.
+template <bool CAUSAL, int POS, bool NAT, int LAY = -1>
 struct TileWalker {
   int s, tt, j;
-  bool bfull;
+  int tend, tfull;  // tiles visited / visited whole in the current block
   int ntile_blk;
 
   __device__ void init(const AttnParams& P) {
     s = 0;
     tt = 0;
     j = 0;
-    bfull = false;
+    tend = 0;
+    tfull = 0;
     ntile_blk = (P.klen + BN - 1) / BN;
   }
 
@@ -206,42 +213,39 @@ struct TileWalker {
     }
   }
 
+  // First tile t in [lo, hi) whose key at local index min(t*BN + off,
+  // klen - 1) has a position above lim (hi if none).
+  __device__ int first_above(const AttnParams& P, int lay, int lo, int hi, int off,
+                             int lim) const {
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (layout_pos(lay, P.N, P.blk, j, min(mid * BN + off, P.klen - 1)) > lim)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    return lo;
+  }
+
   // Advance to the next tile with at least one visible pair.
   __device__ bool next(const AttnParams& P, int dev, int qmin, int qmax, Tile& T) {
     const int lane = threadIdx.x & 63;
     const int lay = LAY >= 0 ? LAY : P.layout;
-    // The common case first, as straight-line code: the next tile inside a
-    // block whose keys are all visible (no mask, nothing to skip).
-    if (FAST && POS != POS_ARRAY && bfull && tt > 0 && tt < ntile_blk) {
-      const int a0 = tt * BN;
-      const int n = min(BN, P.klen - a0);
-      T.start = (int64_t)j * P.klen + a0;
-      T.n = n;
-      T.kp = 0;
-      T.full = n == BN;
-      // positions: for natural-order copies, and for the mask of a ragged
-      // last tile (its keys past n are masked through the general path)
-      if (NAT || (CAUSAL && POS == POS_ANALYTIC && n < BN)) positions(P, lay, a0, n, T);
-      ++tt;
-      return true;
-    }
-    while (s < P.nkblk) {
-      if (tt == 0) {
+    constexpr bool ANALYTIC = CAUSAL && POS == POS_ANALYTIC;
+    for (;;) {
+      if (tt == 0) {  // a new key block
+        if (s >= P.nkblk) return false;
         // ring order (uniform; the first-lane read keeps it scalar, as the
         // remainder is computed in vector registers)
         j = __builtin_amdgcn_readfirstlane(((dev - s) % P.nkblk + P.nkblk) % P.nkblk);
-        bfull = !CAUSAL;
-        if (CAUSAL && POS == POS_ANALYTIC) {
-          const int kf = layout_pos(lay, P.N, P.blk, j, 0);
-          const int kl = layout_pos(lay, P.N, P.blk, j, P.klen - 1);
-          if (kf > qmax) {
-            ++s;
-            continue;
-          }
-          bfull = kl <= qmin;
+        tend = ntile_blk;
+        tfull = CAUSAL ? 0 : ntile_blk;
+        if (ANALYTIC) {
+          tend = first_above(P, lay, 0, ntile_blk, 0, qmax);
+          tfull = first_above(P, lay, 0, tend, BN - 1, qmin);
         }
       }
-      if (tt >= ntile_blk) {
+      if (tt >= tend) {
         ++s;
         tt = 0;
         continue;
@@ -251,35 +255,21 @@ struct TileWalker {
       T.start = (int64_t)j * P.klen + a0;
       T.n = n;
       T.kp = 0;
-      bool full = (n == BN);
-      if (NAT && !(CAUSAL && POS == POS_ANALYTIC))
-        positions(P, lay, a0, n, T);  // natural-order rows (no mask needed)
-      if (CAUSAL && POS == POS_ANALYTIC) {
-        if (!bfull) {
-          const int kf = layout_pos(lay, P.N, P.blk, j, a0);
-          const int kl = layout_pos(lay, P.N, P.blk, j, a0 + n - 1);
-          if (kf > qmax) {  // positions ascend in a block: nothing after is visible
-            ++s;
-            tt = 0;
-            continue;
-          }
-          full = full && (kl <= qmin);
-        }
-        positions(P, lay, a0, n, T);
-      }
+      bool full = n == BN && tt < tfull;
       ++tt;
       if (CAUSAL && POS == POS_ARRAY) {
         const int kp = lane < n ? P.k_pos[T.start + lane] : 0;
         const int kmin = wave_min(lane < n ? kp : INT32_MAX);
         const int kmax = wave_max(lane < n ? kp : INT32_MIN);
         if (kmin > qmax) continue;
-        full = full && (kmax <= qmin);
+        full = n == BN && kmax <= qmin;
         T.kp = kp;
       }
+      // positions: for natural-order copies and for the analytic mask
+      if (NAT || (ANALYTIC && !full)) positions(P, lay, a0, n, T);
       T.full = full;
       return true;
     }
-    return false;
   }
 };
 
@@ -556,8 +546,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     }
   };
 
-  // (the zigzag kernels run out of scalar registers with the fast path)
-  TileWalker<CAUSAL, POS, NAT, LAY, LAY != RA_ZIGZAG> walker;
+  TileWalker<CAUSAL, POS, NAT, LAY> walker;
   walker.init(P);
   Tile cur;
   bool have = walker.next(P, dev, qmin, qmax, cur);
