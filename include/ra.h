@@ -34,7 +34,8 @@
  *   - Scores are s = (q . k) * scale; scale <= 0 selects 1/sqrt(D).
  *   - Causal masking is on global token positions: key j is visible to
  *     query i iff pos(j) <= pos(i) (the diagonal is visible).
- *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *   - `stream` is a hipStream_t (NULL = the null stream), passed as void* so
+ *     that this header needs no HIP header and stays plain C.  Calls are
  *     asynchronous on it; none synchronises the device.
  *   - Every argument is validated on the host before anything is launched;
  *     on error nothing is launched, the call returns a non-zero ra_status and
@@ -162,7 +163,9 @@ ra_status ra_ring(const void* Q, const void* K, const void* V, void* out, float*
 size_t ra_ring_workspace_bytes(const ra_dims* d, int N, ra_layout layout, int device);
 
 /* Layout permutation of rows ("Module 23", "The Causal Imbalance -- and the
- * Striped Fix"): src and dst are [outer, S, row_bytes] byte arrays.
+ * Striped Fix"): src and dst are [outer, S, row_bytes] byte arrays.  Rows are
+ * opaque bytes, so one call moves Q/K/V/out rows (D elements) and lse rows
+ * (one fp32) alike.
  *   inverse == 0: natural -> device order, dst[o][p*blk + a] = src[o][pos(p, a)]
  *   inverse == 1: device -> natural order, dst[o][pos(p, a)] = src[o][p*blk + a]
  * row_bytes must be a positive multiple of 4 (16 or more runs vectorised).
@@ -170,9 +173,11 @@ size_t ra_ring_workspace_bytes(const ra_dims* d, int N, ra_layout layout, int de
 ra_status ra_permute(const void* src, void* dst, int64_t outer, int64_t S, int64_t row_bytes,
                      int N, ra_layout layout, int inverse, void* stream);
 
-/* int32 global positions.  device == -1: pos[i] for every index i of a
- * device-ordered sequence (S entries).  device == p: p's block in its local
- * order (S/N entries). */
+/* int32 global positions, the operands of the causal mask ("Module 23",
+ * "Exact by Construction": key visible iff its position is not after the
+ * query's; "The Causal Imbalance -- and the Striped Fix": the layouts).
+ * device == -1: pos[i] for every index i of a device-ordered sequence
+ * (S entries).  device == p: p's block in its local order (S/N entries). */
 ra_status ra_positions(int32_t* pos, int64_t S, int N, ra_layout layout, int device,
                        void* stream);
 
