@@ -650,9 +650,9 @@ int64_t ra_xcd_plan(const ra_dims* d, int N, ra_layout layout, int causal, int d
   if (!(d->dtype == RA_BF16 && ra::mfma_supports((int)d->D))) return 0;
   ra::AttnParams p = ring_params(d, N, layout, device);
   int rows, per_cu;
-  ra::mfma_geometry((int)d->D, p.qlen, &rows, &per_cu);
+  ra::mfma_geometry((int)d->D, p.qlen, p.Hq / p.Hkv, &rows, &p.gpl, &per_cu);
   p.ntq = (p.qlen + rows - 1) / rows;
-  const int64_t nwg = (int64_t)p.B * p.Hq * p.nqblk * p.ntq;
+  const int64_t nwg = (int64_t)p.B * (p.Hq >> p.gpl) * p.nqblk * p.ntq;
   ra::XcdPlan X;
   const int64_t grid = ra::xcd_plan_for(p, nwg, causal != 0, rows, per_cu, speeds, &X);
   if (grid > 0) {

@@ -6,12 +6,15 @@
 // a denominator l and an unnormalised output o are rescaled by exp(m_old -
 // m_new) and updated with each block's exp(s - m_new) and exp(s - m_new) v.
 //
-// Work split.  A workgroup owns BM = 32*NW query rows of one (batch, query
-// head) and walks the key/value blocks in ring order, 64 keys per tile; each
-// of its NW waves owns 32 query rows (NW = 8 for head dim 128 and query
-// blocks of at least 256 rows: one 512-thread workgroup per CU, two waves per
-// SIMD, each key/value tile shared by 256 query rows; otherwise NW = 4, two
-// workgroups per CU).  Per tile and wave:
+// Work split.  A workgroup owns 32*NW (query row, query head) pairs of one
+// batch and kv head and walks the key/value blocks in ring order, 64 keys per
+// tile; each of its NW waves owns 32 query rows of one head (NW = 8 for head
+// dim 128 and query blocks of at least 256 rows: one 512-thread workgroup per
+// CU, two waves per SIMD, each key/value tile shared by 256 query rows;
+// otherwise NW = 4, two workgroups per CU).  Under grouped-query attention the
+// waves are spread over up to NW query heads of the kv head (the largest power
+// of two dividing Hq / Hkv), all on the same positions: the causal walk then
+// covers a shorter stretch of positions per workgroup.  Per tile and wave:
 //   S^T[64 keys x 32 queries] = K_tile . Q^T   v_mfma_f32_32x32x16_bf16,
 //        A = K rows read from LDS, B = Q^T fragments held in registers;
 //   softmax on S^T: every lane holds 32 scores of ONE query (the other 32 of
@@ -314,13 +317,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     g_xcd_stat[2 * kXcds + x] = 0;
     g_xcd_stat[kXcds + x] = X.tag | stamp40();
   }
+  // A workgroup serves 2^gpl query heads of one kv head over the same R query
+  // rows, one wave per 32 rows of one head: its heads share every K / V tile,
+  // and its rows span 2^gpl times fewer positions than one head over all the
+  // waves would, so the causal bounds of its tile walk are that much tighter.
+  constexpr int LNW = NW == 8 ? 3 : 2;
+  static_assert((1 << LNW) == NW, "4 or 8 waves");
   const int G = P.Hq / P.Hkv;
-  const int hg = (int)(L % G);
-  L /= G;
+  const int wl = LNW - P.gpl;     // log2 of the waves per head
+  const int R = 32 << wl;         // query rows per head
+  const int ngrp = G >> P.gpl;    // workgroups per (kv head, query tile)
+  const int hs = (int)(L % ngrp);
+  L /= ngrp;
   const int nt = P.nqblk * P.ntq;
   int qi, t;
-  item_tile(lay, CAUSAL && POS == POS_ANALYTIC, P.nqblk, P.ntq, NW * 32, P.blk,
-            (int)(L % nt), qi, t);
+  item_tile(lay, CAUSAL && POS == POS_ANALYTIC, P.nqblk, P.ntq, R, P.blk, (int)(L % nt), qi, t);
   L /= nt;
   // Integer division has no scalar form, so the decode above may leave its
   // results in vector registers; they are uniform over the workgroup, and
@@ -330,12 +341,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   const int b = __builtin_amdgcn_readfirstlane((int)(L / P.Hkv));
   qi = __builtin_amdgcn_readfirstlane(qi);
   t = __builtin_amdgcn_readfirstlane(t);
-  const int h = g * G + __builtin_amdgcn_readfirstlane(hg);
+  const int h = g * G + (__builtin_amdgcn_readfirstlane(hs) << P.gpl) + (wave >> wl);
   const int dev = P.dev0 + qi;
 
-  const int a0q = t * (NW * 32);                // first local row of the tile
-  const int nrows = min(NW * 32, P.qlen - a0q);
-  const int la = a0q + wave * 32 + r;           // this lane's local query row
+  const int a0q = t * R;                        // first local row of the tile
+  const int nrows = min(R, P.qlen - a0q);
+  const int la = a0q + (wave & ((1 << wl) - 1)) * 32 + r;  // this lane's local query row
   const bool rvalid = la < P.qlen;
   // the query row in Q / out / lse: device order, or (NAT) the row's natural
   // token position
@@ -863,13 +874,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   }
 }
 
+// log2 of the query heads a workgroup of `nw` waves serves: the largest power
+// of two that divides the group size G = Hq / Hkv, at most nw.
+int heads_log2(int G, int nw) {
+  int l = 0;
+  while ((2 << l) <= nw && G % (2 << l) == 0) ++l;
+  return l;
+}
+
 template <int D, int NW>
 hipError_t launch_d(const AttnParams& p0, bool causal, int pos_mode, bool state_io, bool natural,
                     hipStream_t s) {
   AttnParams p = p0;
-  p.ntq = (p.qlen + NW * 32 - 1) / (NW * 32);
-  const int64_t nwg = (int64_t)p.B * p.Hq * p.nqblk * p.ntq;
-  const int rows = NW * 32, per_cu = NW == 8 ? 1 : 2;
+  p.gpl = heads_log2(p.Hq / p.Hkv, NW);
+  const int rows = (NW * 32) >> p.gpl, per_cu = NW == 8 ? 1 : 2;  // rows per head
+  p.ntq = (p.qlen + rows - 1) / rows;
+  const int64_t nwg = (int64_t)p.B * (p.Hq >> p.gpl) * p.nqblk * p.ntq;
   const bool ring = !state_io && pos_mode != POS_ARRAY;
   XcdPlan X;
   const int64_t ngrid = xcd_prepare(p, nwg, causal, ring, rows, per_cu, s, &X);
@@ -940,9 +960,10 @@ void* xcd_stat_address() {
   return p;
 }
 
-void mfma_geometry(int D, int qlen, int* rows, int* per_cu) {
+void mfma_geometry(int D, int qlen, int G, int* rows, int* gpl, int* per_cu) {
   const int nw = (D == 128 && qlen >= 256) ? 8 : 4;
-  *rows = nw * 32;
+  *gpl = heads_log2(G, nw);
+  *rows = (nw * 32) >> *gpl;
   *per_cu = nw == 8 ? 1 : 2;  // one 8-wave or two 4-wave workgroups share a CU
 }
 

@@ -119,6 +119,8 @@ struct AttnParams {
   int nqblk, qlen, dev0;
   int nkblk, klen;
   int ntq;         // query tiles per query block (kernel specific)
+  int gpl;         // log2 of the query heads of one kv head a workgroup serves
+                   // (matrix-core kernel; 0 elsewhere)
   int layout, N, blk;  // POS_ANALYTIC
   float scale;     // score scale
   float sl2;       // scale * log2(e)
@@ -130,9 +132,11 @@ struct AttnParams {
 hipError_t launch_attn_mfma(const AttnParams& p, int D, bool causal, int pos_mode, bool state_io,
                             bool natural, hipStream_t s);
 bool mfma_supports(int D);
-// Rows per workgroup and resident workgroups per CU of the matrix-core kernel
-// in a ring launch (state kept on chip) over a query block of `qlen` rows.
-void mfma_geometry(int D, int qlen, int* rows, int* per_cu);
+// Geometry of the matrix-core kernel in a ring launch (state kept on chip)
+// over query blocks of `qlen` rows with G = Hq / Hkv query heads per kv head:
+// query rows per head in one workgroup, log2 of the heads it serves, and
+// resident workgroups per CU.
+void mfma_geometry(int D, int qlen, int G, int* rows, int* gpl, int* per_cu);
 // Device address, on the current device, of the XCD stamp array (nullptr on
 // failure).
 void* xcd_stat_address();

@@ -46,13 +46,13 @@ constexpr int kAvgN = 8;                 // measurements averaged (see consume)
 constexpr unsigned kReadAll = 64;        // launches read back one by one, then one in 8
 
 struct Shape {
-  int B, Hq, Hkv, nqblk, qlen, dev0, nkblk, klen, ntq, layout, N, blk, causal, rows, per_cu;
+  int B, Hq, Hkv, nqblk, qlen, dev0, nkblk, klen, ntq, gpl, layout, N, blk, causal, rows, per_cu;
   bool operator==(const Shape& o) const { return memcmp(this, &o, sizeof(Shape)) == 0; }
 };
 
 Shape shape_of(const AttnParams& p, bool causal, int rows, int per_cu) {
-  return Shape{p.B,  p.Hq,     p.Hkv, p.nqblk, p.qlen,       p.dev0, p.nkblk, p.klen,
-               p.ntq, p.layout, p.N,   p.blk,   causal ? 1 : 0, rows,  per_cu};
+  return Shape{p.B,     p.Hq, p.Hkv,    p.nqblk, p.qlen, p.dev0,        p.nkblk, p.klen,
+               p.ntq,   p.gpl, p.layout, p.N,     p.blk,  causal ? 1 : 0, rows,    per_cu};
 }
 
 // Tiles the kernel visits for query tile t of query block qi.  Positions ascend
@@ -84,11 +84,11 @@ double tile_count(const Shape& s, int qi, int t) {
   return n;
 }
 
-// Work of every item in tile units, indexed as the kernel numbers items: query
-// head within its group fastest, then the (query block, query tile) rank of
-// item_tile, then kv head and batch.
+// Work of every item in tile units, indexed as the kernel numbers items: the
+// item's set of query heads within their kv head's group fastest, then the
+// (query block, query tile) rank of item_tile, then kv head and batch.
 std::vector<float> item_work(const Shape& s) {
-  const int G = s.Hq / s.Hkv;
+  const int ngrp = (s.Hq / s.Hkv) >> s.gpl;  // items per (kv head, query tile)
   const int nt = s.nqblk * s.ntq;
   std::vector<float> per((size_t)nt);
   for (int r = 0; r < nt; ++r) {
@@ -96,9 +96,9 @@ std::vector<float> item_work(const Shape& s) {
     item_tile(s.layout, s.causal != 0, s.nqblk, s.ntq, s.rows, s.blk, r, qi, t);
     per[(size_t)r] = (float)(tile_count(s, qi, t) + kItemFixed);
   }
-  const int64_t W = (int64_t)s.B * s.Hq * nt;
+  const int64_t W = (int64_t)s.B * s.Hkv * ngrp * nt;
   std::vector<float> wk((size_t)W);
-  for (int64_t L = 0; L < W; ++L) wk[(size_t)L] = per[(size_t)((L / G) % nt)];
+  for (int64_t L = 0; L < W; ++L) wk[(size_t)L] = per[(size_t)((L / ngrp) % nt)];
   return wk;
 }
 
