@@ -738,6 +738,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
     });
     static_for<NS>([&](auto I) __attribute__((always_inline)) {
       constexpr int st = decltype(I)::value;
+      // Issue priority: raised while the wave's softmax runs beside its
+      // MFMAs (sections 2 and 3), normal in the MFMA-only sections (1 and 4):
+      // where the two waves of a SIMD compete, the one with vector work
+      // pending issues first.
+      if constexpr (st == 0 || st == 2 * NC + NSTEP) __builtin_amdgcn_s_setprio(0);
+      if constexpr (st == NC) __builtin_amdgcn_s_setprio(1);
       if constexpr (st + PD < NS) opd[(st + PD) % (PD + 1)] = operand(st + PD);
       __builtin_amdgcn_sched_barrier(0);
       const u32x4 a = opd[st % (PD + 1)];
