@@ -707,6 +707,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   // boundaries (MFMA and VALU of one wave overlap in hardware; the fences
   // keep the compiler from reordering across the steps).
   constexpr int PD = 3;  // operand read distance, in MFMAs
+  // Step at which the next tile's copy is issued.  Contiguous and non-causal
+  // rings find nearly every K / V tile in L2 (95 % of L2 requests hit) and
+  // issue it at the start of the P.V steps, away from the operand reads at
+  // the tile's start.  Striped rings (a quarter of L2 requests miss on the
+  // 64K-token ring), zigzag ones (a 1M-token device share reads its K / V
+  // from memory many times over) and the state-in-HBM steps (few tiles per
+  // workgroup, each first read from memory) issue it halfway through the
+  // first QK^T section, which leaves the copy most of a tile to land.
+  constexpr int kCopyStep =
+      (!STATE_IO && (!CAUSAL || (POS == POS_ANALYTIC && LAY == RA_CONTIGUOUS))) ? 2 * NC
+                                                                                : NC / 2;
   auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& ct,
                   const Tile& nt, bool have_next) {
     const lds_t* Kb = cb;
@@ -749,7 +760,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       const u32x4 a = opd[st % (PD + 1)];
       if constexpr (st < NC) {
         s0 = mfma(a, qf[st], st == 0 ? f32x16{} : s0);
-        if constexpr (st == NC / 2) issue_tile(have_next ? nt : ct, nb);  // last tile re-copies itself
       } else if constexpr (st < 2 * NC) {
         constexpr int c = st - NC;
         s1 = mfma(a, qf[c], c == 0 ? f32x16{} : s1);
@@ -774,6 +784,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
         constexpr int v = st - 2 * NC - NSTEP, hh = v / NDB, db = v % NDB;
         o[db] = mfma(a, pf[1][hh], o[db]);
       }
+      if constexpr (st == kCopyStep) issue_tile(have_next ? nt : ct, nb);  // last tile re-copies itself
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (st == NC - 1) {
         if (__builtin_expect(!ct.full, 0)) mask_half(s0, 0, ct);
