@@ -783,6 +783,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
       } else {
         constexpr int v = st - 2 * NC - NSTEP, hh = v / NDB, db = v % NDB;
         o[db] = mfma(a, pf[1][hh], o[db]);
+        // Ring kernels: the second P register of half 1 (elements 8..15) is
+        // packed here, beside the MFMAs that only use the first one, rather
+        // than between the two P.V sections (the empty asm keeps each pack
+        // in its step).
+        if constexpr (!STATE_IO && v < NDB) {
+#pragma unroll
+          for (int j = 4 + v * 4 / NDB; j < 4 + (v + 1) * 4 / NDB; ++j) {
+            unsigned pk = pack2(pv1[2 * j], pv1[2 * j + 1]);
+            asm volatile("" : "+v"(pk));
+            pf[1][1][j - 4] = pk;
+          }
+        }
       }
       if constexpr (st == kCopyStep) issue_tile(have_next ? nt : ct, nb);  // last tile re-copies itself
       __builtin_amdgcn_sched_barrier(0);
@@ -809,7 +821,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
         } else {
           ps1 += ps1b;
           softmax_check(s1, pv1, ps1);
-          pack_half(pv1, pf[1][0], pf[1][1]);
+          pf[1][0] = u32x4{pack2(pv1[0], pv1[1]), pack2(pv1[2], pv1[3]), pack2(pv1[4], pv1[5]),
+                           pack2(pv1[6], pv1[7])};
         }
       }
       __builtin_amdgcn_sched_barrier(0);
