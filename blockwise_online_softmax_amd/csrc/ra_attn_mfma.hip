@@ -707,17 +707,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   // boundaries (MFMA and VALU of one wave overlap in hardware; the fences
   // keep the compiler from reordering across the steps).
   constexpr int PD = 3;  // operand read distance, in MFMAs
-  // Step at which the next tile's copy is issued.  Contiguous and non-causal
-  // rings find nearly every K / V tile in L2 (95 % of L2 requests hit) and
-  // issue it at the start of the P.V steps, away from the operand reads at
-  // the tile's start.  Striped rings (a quarter of L2 requests miss on the
-  // 64K-token ring), zigzag ones (a 1M-token device share reads its K / V
-  // from memory many times over) and the state-in-HBM steps (few tiles per
+  // Step at which the next tile's copy is issued.  Contiguous, striped and
+  // non-causal rings issue it at the start of the P.V steps, away from the
+  // operand reads at the tile's start; half a tile is enough for it to land
+  // (a quarter is not).  Zigzag rings (a 1M-token device share reads its K /
+  // V from memory many times over) and the state-in-HBM steps (few tiles per
   // workgroup, each first read from memory) issue it halfway through the
   // first QK^T section, which leaves the copy most of a tile to land.
   constexpr int kCopyStep =
-      (!STATE_IO && (!CAUSAL || (POS == POS_ANALYTIC && LAY == RA_CONTIGUOUS))) ? 2 * NC
-                                                                                : NC / 2;
+      (!STATE_IO &&
+       (!CAUSAL || (POS == POS_ANALYTIC && (LAY == RA_CONTIGUOUS || LAY == RA_STRIPED))))
+          ? 2 * NC
+          : NC / 2;
   auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& ct,
                   const Tile& nt, bool have_next) {
     const lds_t* Kb = cb;
