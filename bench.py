@@ -367,9 +367,51 @@ def step_sweep(args):
         torch.cuda.empty_cache()
 
 
+def interleaved_whole_rings(qd, kd, vd, out, lse, N, layouts, args, stream):
+    """Whole causal rings of every layout on the same tensors, timed in
+    interleaved rounds (the layout order rotates from round to round) after a
+    common warm-up, so that the clock's drift over the run falls on every
+    layout alike.  Per layout: mean, median and minimum over all its timed
+    launches (HIP events on the launch stream)."""
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+
+    calls = {}
+    for layout in layouts:
+        nws = ra.ra_ring_workspace_bytes(qd, kd, N, layout, -1)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        calls[layout] = (lambda L=layout, W=ws: ra.ra_ring(qd, kd, vd, out, lse, N, L, True, -1, W,
+                                                          stream=stream))
+    for layout in layouts:  # warm-up: every layout, then until 0.5 s have passed
+        for _ in range(args.warmup):
+            calls[layout]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:
+        for layout in layouts:
+            calls[layout]()
+        torch.cuda.synchronize()
+    rounds, per = max(3, args.steps), 2
+    ms = {layout: [] for layout in layouts}
+    for r in range(rounds):
+        order = layouts[r % len(layouts):] + layouts[:r % len(layouts)]
+        for layout in order:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(per)]
+            for a, b in ev:
+                a.record(stream)
+                calls[layout]()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms[layout] += [a.elapsed_time(b) for a, b in ev]
+    return {layout: ms_stats(v) for layout, v in ms.items()}
+
+
 def layout_balance(args):
     """The 64K-token causal ring (32/8 heads, D=128, N=8) under each layout:
-    the whole ring on one GPU (device = -1, permute + fused ring + un-permute),
+    the whole ring on one GPU (device = -1; the three layouts timed in
+    interleaved rounds on the same tensors),
     the permute and un-permute passes alone, and each virtual device's share
     (device = p) whose maximum is the makespan of an N-GPU ring that overlaps
     its key/value passes."""
@@ -388,12 +430,10 @@ def layout_balance(args):
     stream = torch.cuda.current_stream()
     out = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
-    for layout in ("contiguous", "striped", "zigzag"):
-        nws = ra.ra_ring_workspace_bytes(qd, kd, N, layout, -1)
-        ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
-        st_whole = timed(lambda: ra.ra_ring(qd, kd, vd, out, lse, N, layout, True, -1, ws,
-                                            stream=stream), args.steps, args.warmup, stream,
-                         stats=True)
+    layouts = ("contiguous", "striped", "zigzag")
+    whole = interleaved_whole_rings(qd, kd, vd, out, lse, N, layouts, args, stream)
+    for layout in layouts:
+        st_whole = whole[layout]
         t_whole = st_whole["mean"]
         rec = {"metric": "causal ring layout balance (64K tokens, N=8)", "layout": layout,
                "whole_ring_ms": round(t_whole, 3), "whole_ring_ms_median": st_whole["median"],
@@ -437,7 +477,7 @@ def layout_balance(args):
                     "tokens_per_s_one_gpu": round(S / (t_whole * 1e-3), 1),
                     "tokens_per_s_projected_ring": round(S / (mk * 1e-3), 1)})
         print(json.dumps(rec), flush=True)
-        del qp, kp, vp, ws
+        del qp, kp, vp
         torch.cuda.empty_cache()
 
 
