@@ -707,18 +707,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnParams P, Xcd
   // boundaries (MFMA and VALU of one wave overlap in hardware; the fences
   // keep the compiler from reordering across the steps).
   constexpr int PD = 3;  // operand read distance, in MFMAs
-  // Step at which the next tile's copy is issued.  Contiguous, striped and
-  // non-causal rings issue it at the start of the P.V steps, away from the
-  // operand reads at the tile's start; half a tile is enough for it to land
-  // (a quarter is not).  Zigzag rings (a 1M-token device share reads its K /
-  // V from memory many times over) and the state-in-HBM steps (few tiles per
-  // workgroup, each first read from memory) issue it halfway through the
-  // first QK^T section, which leaves the copy most of a tile to land.
-  constexpr int kCopyStep =
-      (!STATE_IO &&
-       (!CAUSAL || (POS == POS_ANALYTIC && (LAY == RA_CONTIGUOUS || LAY == RA_STRIPED))))
-          ? 2 * NC
-          : NC / 2;
+  // Step at which the next tile's copy is issued.  Ring kernels issue it at
+  // the start of the P.V steps, away from the operand reads at the tile's
+  // start; half a tile is enough for it to land (a quarter is not).  The
+  // later issue also keeps the workgroups of an XCD that stream the same K /
+  // V in step: a workgroup that runs ahead of the others is the first to
+  // miss in L2 and waits a little at its tile's end, the others then find
+  // those tiles in L2.  (Issued halfway through the first QK^T section, the
+  // latency was hidden, the 32 workgroups of an XCD drifted apart over a
+  // 1M-token device share, and it fetched 0.7-0.9 TB per launch instead of
+  // 139 GB.)  The state-in-HBM steps (few tiles per workgroup, each first
+  // read from memory) keep the early issue.
+  constexpr int kCopyStep = !STATE_IO ? 2 * NC : NC / 2;
   auto tile = [&](const lds_t* __restrict__ cb, lds_t* __restrict__ nb, const Tile& ct,
                   const Tile& nt, bool have_next) {
     const lds_t* Kb = cb;
