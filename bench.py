@@ -77,17 +77,24 @@ def layout_pos(layout, N, blk, dev, a):
     return dev * blk + a
 
 
-def executed_pairs(S, N, layout, causal, device, D, tile_keys=64):
+def executed_pairs(S, N, layout, causal, device, D, G=1, tile_keys=64):
     """(query, key) pairs the matrix-core ring kernel computes per query head,
     masked ones included: every (query tile, key tile) it visits in full.  A
-    query tile is 256 rows (D = 128 and blocks of >= 256 rows) or 128; key
-    tiles are 64 keys.  Positions ascend inside a device block, so under the
-    causal mask a key block is skipped when its first key follows the tile's
-    last query, and otherwise runs up to its last tile that starts at or
-    before that query.  The excess over the visible pairs is the work done on
-    masked parts of diagonal tiles."""
+    workgroup has 8 wavefronts (D = 128 and blocks of >= 256 rows) or 4, of 32
+    rows each, spread over 2^gpl query heads of one kv head (the largest power
+    of two dividing G = Hq / Hkv, at most the wavefront count) on the same
+    positions, so a query tile is 32 x waves / 2^gpl positions; key tiles are
+    64 keys.  Positions ascend inside a device block, so under the causal
+    mask a key block is skipped when its first key follows the tile's last
+    query, and otherwise runs up to its last tile that starts at or before
+    that query.  The excess over the visible pairs is the work done on masked
+    parts of diagonal tiles."""
     blk = S // N
-    rows = 256 if (D == 128 and blk >= 256) else 128
+    nw = 8 if (D == 128 and blk >= 256) else 4
+    gpl = 0
+    while (2 << gpl) <= nw and G % (2 << gpl) == 0:
+        gpl += 1
+    rows = (nw * 32) >> gpl
     devs = range(N) if device < 0 else [device]
     ntile = -(-blk // tile_keys)
     tile_first = np.arange(ntile) * tile_keys
@@ -135,10 +142,78 @@ def parse():
     ap.add_argument("--xcd-ab", action="store_true",
                     help="the --workload ring with the even split over the 8 XCDs against the split "
                          "sized by the measured XCD speeds (both frozen), alternating; one JSON line")
+    ap.add_argument("--tile-mix", action="store_true",
+                    help="timing probe of the attention tile loop's instruction mix (MFMA, LDS "
+                         "operand reads, softmax) without copies or barriers, beside the gqa32k "
+                         "ring; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (contiguous ra_permute) so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
     return ap.parse_args()
+
+
+def tile_mix(args):
+    """The attention tile loop's instruction mix in isolation (libra_probe.so,
+    tile_mix_kernel): one workgroup per CU issuing v_mfma_f32_32x32x16_bf16 on
+    data-like bf16 operands, with or without the LDS operand reads and the
+    softmax work of the ring kernel, in launches of ~35 ms so that the clock
+    settles; the five configurations run in rotating rounds.  Beside it, the
+    gqa32k ring (even XCD split) in the same units: MFMAs issued per
+    microsecond per CU (executed FLOPs / 32768)."""
+    import ctypes
+
+    import torch
+
+    import blockwise_online_softmax_amd as ra
+    import workloads
+
+    lib = ctypes.CDLL(os.path.join(HERE, "blockwise_online_softmax_amd", "libra_probe.so"))
+    fn = lib.ra_probe_tile_mix
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_longlong),
+                   ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ["mfma only (8 waves)", "mfma + softmax (8 waves)",
+             "mfma + 1 KB LDS per MFMA (8 waves)",
+             "mfma + 1 KB LDS per MFMA + softmax (8 waves: the ring kernel's mix)",
+             "mfma + 0.5 KB LDS per MFMA + softmax (4 waves of 64 query rows)"]
+    iters = 110000
+
+    def run(cfg):
+        ms, n = ctypes.c_float(), ctypes.c_longlong()
+        rc = fn(cfg, cus, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(ms),
+                ctypes.byref(n), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"ra_probe_tile_mix failed with HIP error {rc}")
+        return n.value / (ms.value * 1e3)
+
+    for cfg in range(len(names)):  # warm-up
+        run(cfg)
+    rates = {c: [] for c in range(len(names))}
+    for r in range(3):
+        for i in range(len(names)):
+            cfg = (i + r) % len(names)
+            rates[cfg].append(run(cfg))
+    # the gqa32k ring in the same units
+    wkey, layout, device = WORKLOADS["gqa32k"]
+    cfgw = workloads.WORKLOADS[wkey]
+    q, k, v = (t.cuda() for t in workloads.workload_inputs(wkey))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    ms = timed(lambda: ra.ra_ring(q, k, v, out, lse, cfgw["N"], layout, True, -1, None,
+                                  stream=stream), 10, 5, stream, min_warm_s=0.5)
+    exec_flops = 4.0 * cfgw["D"] * cfgw["Hq"] * executed_pairs(
+        cfgw["S"], cfgw["N"], layout, True, -1, cfgw["D"], G=cfgw["Hq"] // cfgw["Hkv"])
+    ring_rate = exec_flops / 32768.0 / cus / (ms * 1e3)
+    res = {names[c]: round(float(np.median(v)), 1) for c, v in rates.items()}
+    print(json.dumps({"metric": "MFMAs per microsecond per CU (tile-loop mix probe)",
+                      "probe": res, "gqa32k_ring": round(ring_rate, 1),
+                      "gqa32k_ring_ms": round(ms, 3),
+                      "ring_over_its_mix": round(ring_rate / res[names[3]], 3),
+                      "launches_per_config": 3, "iters": iters, "cus": cus}), flush=True)
 
 
 def copy_calibration():
@@ -671,6 +746,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.tile_mix:
+        tile_mix(args)
+        return
     if args.step_sweep:
         step_sweep(args)
         return
@@ -751,7 +829,8 @@ def main():
     xcd = {"mode": args.xcd, "speeds": [round(x, 4) for x in speeds], "measurements": nmeas,
            "workgroups": grid, "items_per_xcd": M, "items_moved": int(sum(dcnt))}
     ra.ra_xcd_speeds(None, set=True)
-    exec_flops = 4.0 * D * cfg["B"] * Hq * executed_pairs(S, N, layout, causal, device, D)
+    exec_flops = 4.0 * D * cfg["B"] * Hq * executed_pairs(S, N, layout, causal, device, D,
+                                                          G=Hq // Hkv)
     ceiling = mfma_ceiling()
     ceiling["attention_kernel_frac_of_ceiling"] = round(kern_tflops / ceiling["tflops"], 4)
     cpu = None
