@@ -72,22 +72,29 @@ __host__ __device__ inline int64_t xcd_item(const XcdPlan& X, int64_t w) {
 }
 
 // Query block qi and query tile t of the r-th item (r < nqblk * ntq, tiles of
-// `rows` rows, blocks of blk rows).  The tiles of one block stay together:
-// they walk the key blocks in the same ring order, so the CUs of an XCD that
-// run them at the same time share K/V tiles in its L2.  Blocks and tiles go
-// in descending order, which under the causal mask is longest-first for
-// contiguous blocks (block p holds p*blk ..) and near it for striped ones
-// (block p holds p, p+N, ..).  Zigzag (block p holds chunk p, then chunk
-// 2N-1-p), causal: the tiles that reach the second chunk, blocks ascending,
-// then the first-chunk tiles, blocks descending, tiles descending within a
-// block; that is longest-first by last query position.
+// `rows` rows, blocks of blk rows), longest-first under the causal mask, so
+// that the last items an XCD runs are its shortest:
+//  * contiguous (block p holds p*blk ..): blocks, then tiles, descending.  The
+//    tiles of one block stay together: they walk the key blocks in the same
+//    ring order, so the CUs of an XCD that run them at the same time share
+//    K/V tiles in its L2.  Non-causal rings of any layout take this order.
+//  * striped (block p holds p, p+N, ..): a tile's work depends on its index
+//    within the block, not on the block, so tiles descending, and within a
+//    tile index blocks descending.  (Blocks first would give every block's
+//    list its own long-to-short run, and long items would still start near
+//    the end.)
+//  * zigzag (block p holds chunk p, then chunk 2N-1-p): the tiles that reach
+//    the second chunk, blocks ascending, then the first-chunk tiles, blocks
+//    descending, tiles descending within a block; that is longest-first by
+//    last query position.
 //
 // Written without branches: a branch on the layout here changes how the
 // compiler allocates the kernel's scalar registers, and the tile loop's walker
 // then moves to vector registers.
 __host__ __device__ inline void item_tile(int layout, bool causal, int nqblk, int ntq, int rows,
                                           int blk, int r, int& qi, int& t) {
-  const int tc = ntq - 1 - r % ntq, qc = nqblk - 1 - r / ntq;  // contiguous, striped
+  const int tc = ntq - 1 - r % ntq, qc = nqblk - 1 - r / ntq;    // contiguous
+  const int ts = ntq - 1 - r / nqblk, qs = nqblk - 1 - r % nqblk;  // striped
   const int t1 = (blk >> 1) / rows;  // zigzag: tiles wholly inside the first chunk
   const int n2 = ntq - t1;           // and tiles that reach the second chunk
   const bool second = t1 == 0 || r < nqblk * n2;
@@ -95,8 +102,9 @@ __host__ __device__ inline void item_tile(int layout, bool causal, int nqblk, in
   const int tz = second ? ntq - 1 - r % n2d : t1 - 1 - r1 % t1d;
   const int qz = second ? r / n2d : nqblk - 1 - r1 / t1d;
   const bool zz = causal && layout == RA_ZIGZAG;
-  t = zz ? tz : tc;
-  qi = zz ? qz : qc;
+  const bool sp = causal && layout == RA_STRIPED;
+  t = zz ? tz : (sp ? ts : tc);
+  qi = zz ? qz : (sp ? qs : qc);
 }
 
 // One launch of an attention kernel.  The query side is `nqblk` blocks of
