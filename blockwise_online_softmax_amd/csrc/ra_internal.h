@@ -34,12 +34,13 @@ enum PosMode : int {
 // its own L2).  The hardware hands workgroup w to XCD w % 8 as that XCD's slot
 // w / 8.  Work items are numbered XCD-major: XCD x owns items x*M .. x*M+M-1,
 // longest first.  XCD x first runs entries dbeg[x] .. dbeg[x]+dcnt[x]-1 of the
-// donated list (the items the XCDs do not keep, XCD after XCD, each in its own
-// order), then the first keep[x] of its own items; later slots have no item.
-// An XCD that gives items away receives none, so every XCD's list ends with
-// its own shortest items.  keep = M and dcnt = 0 everywhere is the fixed
-// XCD-major order.  An item is computed the same way on any XCD, so a plan
-// changes timing, never results.
+// donated list (the first M - keep[y] items of every XCD y, the longest it
+// gives away, XCD after XCD, each in its own order), then the last keep[x] of
+// its own items; later slots have no item.  An XCD that gives items away
+// receives none, and every XCD's list ends with its own shortest items, which
+// fill the last gaps of its CUs.  keep = M and dcnt = 0 everywhere is the
+// fixed XCD-major order.  An item is computed the same way on any XCD, so a
+// plan changes timing, never results.
 constexpr int kXcds = 8;
 struct XcdPlan {
   int M;  // items per XCD; 0: no split (item = workgroup index)
@@ -65,10 +66,10 @@ __host__ __device__ inline int64_t xcd_item(const XcdPlan& X, int64_t w) {
       idx -= X.M - X.keep[y];
       ++y;
     }
-    return (int64_t)y * X.M + X.keep[y] + idx;
+    return (int64_t)y * X.M + idx;
   }
   const int own = sl - X.dcnt[x];
-  return own < X.keep[x] ? (int64_t)x * X.M + own : -1;
+  return own < X.keep[x] ? (int64_t)x * X.M + (X.M - X.keep[x]) + own : -1;
 }
 
 // Query block qi and query tile t of the r-th item (r < nqblk * ntq, tiles of

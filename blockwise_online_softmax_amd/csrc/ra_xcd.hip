@@ -11,9 +11,11 @@
 // mode is chosen), and a later call reads them once that copy has completed
 // (never waiting for it).  Work over running time gives each XCD's speed, and
 // their running average sizes the next launches' split.  Under either mode a
-// slow XCD hands the tail of its longest-first item list to faster ones, and
-// the split is kept only if a simulation of each XCD's list schedule says it
-// ends sooner than the fixed one.  Nothing here changes what any item computes.
+// slow XCD hands the head of its longest-first item list to faster ones, which
+// run those items first; every XCD keeps its own shortest items to end its
+// list.  The split is kept only if a simulation of each XCD's list schedule
+// says it ends sooner than the fixed one.  Nothing here changes what any item
+// computes.
 #include <limits.h>
 #include <math.h>
 #include <stdlib.h>
@@ -159,12 +161,61 @@ bool plan_valid(const XcdPlan& X, int64_t W, int64_t grid) {
   return n == W;
 }
 
-// The split for per-XCD speeds fin (any positive scale): each XCD's target is
-// the total work times its share of the speed; an XCD above its target keeps
-// the head of its list up to the target, and the items it drops go, in order,
-// to the XCDs below theirs, which run them before their own.  Falls back to the
-// fixed split unless the simulation says the new one ends sooner.
+// The split for per-XCD shares of the work `tgt` (in tile units, gaps
+// included, summing to the whole launch): an XCD above its share gives away
+// the head of its list (its longest items) and keeps the tail that fits its
+// share; the items given away go, in order, to the XCDs below theirs, which
+// run them before their own.  An XCD that keeps its whole list and is below
+// its share receives; the last such XCD takes whatever is left.  Returns
+// false when nothing moves.
+bool plan_for_shares(const std::vector<float>& wk, int M, const double* tgt, Planned& pl) {
+  fixed_plan(pl.xp, M);
+  double kept[kXcds];
+  std::vector<int64_t> donated;
+  for (int x = 0; x < kXcds; ++x) {
+    double own = 0;
+    for (int s = 0; s < M; ++s) own += wk[(size_t)x * M + s] + kItemGap;
+    kept[x] = own;
+    if (own <= tgt[x]) continue;
+    double cum = 0;
+    int j = M;  // keep items j .. M-1
+    while (j > 0 && cum + 0.5 * (wk[(size_t)x * M + j - 1] + kItemGap) < tgt[x])
+      cum += wk[(size_t)x * M + --j] + kItemGap;
+    pl.xp.keep[x] = M - j;
+    kept[x] = cum;
+    for (int s = 0; s < j; ++s) donated.push_back((int64_t)x * M + s);
+  }
+  if (donated.empty()) return false;
+  size_t pos = 0;
+  int last = -1;
+  for (int x = 0; x < kXcds; ++x) {
+    pl.xp.dbeg[x] = (int)pos;
+    const double need = tgt[x] - kept[x];
+    if (pl.xp.keep[x] < M || need <= 0) continue;
+    double got = 0;
+    while (pos < donated.size() && got + 0.5 * (wk[(size_t)donated[pos]] + kItemGap) < need) {
+      got += wk[(size_t)donated[pos++]] + kItemGap;
+      ++pl.xp.dcnt[x];
+    }
+    last = x;
+  }
+  if (last < 0) return false;
+  pl.xp.dcnt[last] += (int)(donated.size() - pos);  // its slice ends where the rest begins
+  int64_t slots_max = 0;
+  for (int x = 0; x < kXcds; ++x)
+    slots_max = std::max<int64_t>(slots_max, pl.xp.keep[x] + pl.xp.dcnt[x]);
+  pl.grid = slots_max * kXcds;
+  return true;
+}
+
+// The split for per-XCD speeds fin (any positive scale).  The first shares
+// are the whole work times each XCD's share of the speed.  Each round then
+// simulates the XCDs' list schedules and scales every share by the mean
+// simulated finish over that XCD's own (an XCD that ends late gets less, one
+// that ends early more).  The plan that ends soonest is kept, if it ends
+// sooner than the fixed split.
 Planned make_plan(const std::vector<float>& wk, int M, const float* fin, int slots) {
+  constexpr int kRounds = 8;
   double f[kXcds], fs = 0;
   for (int x = 0; x < kXcds; ++x) {
     f[x] = fin[x] > 0.f ? fin[x] : 1.0;
@@ -175,48 +226,29 @@ Planned make_plan(const std::vector<float>& wk, int M, const float* fin, int slo
   fixed.grid = (int64_t)M * kXcds;
   const double t_fixed = finish(fixed, wk, f, slots);
 
-  double own[kXcds], kept[kXcds], total = 0;
-  for (int x = 0; x < kXcds; ++x) {
-    own[x] = 0;
-    for (int s = 0; s < M; ++s) own[x] += wk[(size_t)x * M + s];
-    total += own[x];
-  }
-  Planned pl;
-  fixed_plan(pl.xp, M);
-  std::vector<int64_t> donated;
-  for (int x = 0; x < kXcds; ++x) {
-    const double target = total * f[x] / fs;
-    kept[x] = own[x];
-    if (own[x] <= target) continue;
-    double cum = 0;
-    int k = 0;
-    while (k < M && cum + 0.5 * wk[(size_t)x * M + k] < target) cum += wk[(size_t)x * M + k++];
-    pl.xp.keep[x] = k;
-    kept[x] = cum;
-    for (int s = k; s < M; ++s) donated.push_back((int64_t)x * M + s);
-  }
-  if (donated.empty()) return fixed;
-  size_t pos = 0;
-  int last = -1;
-  for (int x = 0; x < kXcds; ++x) {
-    pl.xp.dbeg[x] = (int)pos;
-    const double need = total * f[x] / fs - kept[x];
-    if (pl.xp.keep[x] < M || need <= 0) continue;
-    double got = 0;
-    while (pos < donated.size() && got + 0.5 * wk[(size_t)donated[pos]] < need) {
-      got += wk[(size_t)donated[pos++]];
-      ++pl.xp.dcnt[x];
+  double total = 0;
+  for (size_t i = 0; i < wk.size(); ++i) total += wk[i] + kItemGap;
+  double tgt[kXcds];
+  for (int x = 0; x < kXcds; ++x) tgt[x] = total * f[x] / fs;
+  Planned best = fixed;
+  double t_best = t_fixed;
+  for (int round = 0; round < kRounds; ++round) {
+    Planned pl;
+    if (!plan_for_shares(wk, M, tgt, pl)) break;
+    const double t = finish(pl, wk, f, slots);
+    if (t < t_best && plan_valid(pl.xp, (int64_t)M * kXcds, pl.grid)) {
+      best = pl;
+      t_best = t;
     }
-    last = x;
+    double mean = 0, sum = 0;
+    for (int x = 0; x < kXcds; ++x) mean += pl.ms[x] / f[x] / kXcds;
+    for (int x = 0; x < kXcds; ++x) {
+      tgt[x] *= mean / (pl.ms[x] / f[x]);
+      sum += tgt[x];
+    }
+    for (int x = 0; x < kXcds; ++x) tgt[x] *= total / sum;
   }
-  if (last < 0) return fixed;
-  pl.xp.dcnt[last] += (int)(donated.size() - pos);  // its slice ends where the rest begins
-  int64_t slots_max = 0;
-  for (int x = 0; x < kXcds; ++x)
-    slots_max = std::max<int64_t>(slots_max, pl.xp.keep[x] + pl.xp.dcnt[x]);
-  pl.grid = slots_max * kXcds;
-  const double t_plan = finish(pl, wk, f, slots);
-  if (t_plan < t_fixed * 0.998 && plan_valid(pl.xp, (int64_t)M * kXcds, pl.grid)) return pl;
+  if (t_best < t_fixed * 0.998) return best;
   return fixed;
 }
 

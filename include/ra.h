@@ -196,16 +196,16 @@ int64_t ra_layout_position(int64_t S, int N, ra_layout layout, int device, int64
  * XCD an equal share; ra_ring then keeps no host state, takes no lock and
  * enqueues nothing but the kernel.  The XCDs of one GPU run a few percent
  * apart, so a caller may ask for a split by per-XCD speeds, given or measured
- * (ra_xcd_speeds): a slow XCD then hands the last (shortest) items of its list
- * to faster ones when a simulation of the schedule says the launch ends
- * sooner.  Results are the same bit for bit under any split. */
+ * (ra_xcd_speeds): a slow XCD then hands the first (longest) items of its
+ * list to faster ones, which run them first, when a simulation of the
+ * schedule says the launch ends sooner.  Results are the same bit for bit under any split. */
 
 /* The split ra_ring would use for this ring under per-XCD speeds speeds[8]
  * (relative, any positive scale).  Host only.  plan receives 25 ints: M (items
  * per XCD; XCD x owns items x*M .. x*M+M-1, longest first), keep[8], dbeg[8]
  * and dcnt[8].  XCD x, slot by slot, first runs entries dbeg .. dbeg+dcnt-1 of
- * the donated list (the items past every XCD's keep count, XCD after XCD),
- * then its own first keep items; slot w / 8 of XCD w % 8 is workgroup w.
+ * the donated list (the first M - keep items of every XCD, XCD after XCD),
+ * then its own last keep items; slot w / 8 of XCD w % 8 is workgroup w.
  * Returns the grid size in workgroups (8*M with keep = M and dcnt = 0 for the
  * equal split); 0, with plan zeroed, for a launch that is never split (fewer
  * than 64 items per XCD, or not the matrix-core kernel); -1 (and sets

@@ -306,9 +306,9 @@ def _xcd_item(M, keep, dbeg, dcnt, w):
         while y < 7 and idx >= M - keep[y]:
             idx -= M - keep[y]
             y += 1
-        return y * M + keep[y] + idx
+        return y * M + idx
     own = sl - dcnt[x]
-    return x * M + own if own < keep[x] else -1
+    return x * M + (M - keep[x]) + own if own < keep[x] else -1
 
 
 def _plan(B, Hq, Hkv, S, D, N, layout, causal, device=-1, speeds=None, dtype=torch.bfloat16):
@@ -333,11 +333,12 @@ def test_xcd_plan_is_a_bijection(layout, causal, device):
     items = [_xcd_item(M, keep, dbeg, dcnt, w) for w in range(grid)]
     got = sorted(i for i in items if i >= 0)
     assert got == list(range(W))
-    # an XCD's own items follow the ones it receives, in their longest-first
-    # order; an XCD that gives items away receives none
+    # an XCD's own items (the last keep[x] of its longest-first list, so its
+    # shortest) follow the ones it receives; an XCD that gives items away
+    # receives none
     for x in range(8):
         own = [items[(dcnt[x] + s) * 8 + x] for s in range(keep[x])]
-        assert own == [x * M + s for s in range(keep[x])]
+        assert own == [x * M + (M - keep[x]) + s for s in range(keep[x])]
         assert keep[x] == M or dcnt[x] == 0
 
 
