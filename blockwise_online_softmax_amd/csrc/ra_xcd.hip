@@ -240,10 +240,18 @@ Planned make_plan(const std::vector<float>& wk, int M, const float* fin, int slo
       best = pl;
       t_best = t;
     }
+    // (an XCD left without items keeps its share)
     double mean = 0, sum = 0;
-    for (int x = 0; x < kXcds; ++x) mean += pl.ms[x] / f[x] / kXcds;
+    int busy = 0;
+    for (int x = 0; x < kXcds; ++x)
+      if (pl.ms[x] > 0) {
+        mean += pl.ms[x] / f[x];
+        ++busy;
+      }
+    if (busy == 0) break;
+    mean /= busy;
     for (int x = 0; x < kXcds; ++x) {
-      tgt[x] *= mean / (pl.ms[x] / f[x]);
+      if (pl.ms[x] > 0) tgt[x] *= mean / (pl.ms[x] / f[x]);
       sum += tgt[x];
     }
     for (int x = 0; x < kXcds; ++x) tgt[x] *= total / sum;

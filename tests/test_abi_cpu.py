@@ -342,6 +342,22 @@ def test_xcd_plan_is_a_bijection(layout, causal, device):
         assert keep[x] == M or dcnt[x] == 0
 
 
+@pytest.mark.parametrize("speeds", [
+    [1, 1, 1, 1, 1, 1, 1, 0.05],          # one XCD nearly stalled: it may keep nothing
+    [10, 1, 1, 1, 1, 1, 1, 1],            # one XCD far faster than the rest
+    [1, 2, 1, 2, 1, 2, 1, 2]])
+def test_xcd_plan_extreme_speeds_stay_a_bijection(speeds):
+    """Speeds far outside the measured range still give a plan that maps the
+    grid one-to-one onto the items (or the fixed split)."""
+    S, W = 32768, 32 * (32768 // 256)
+    grid, M, keep, dbeg, dcnt = _plan(1, 32, 8, S, 128, 8, "contiguous", True, -1, speeds)
+    assert M * 8 == W and grid % 8 == 0
+    items = [_xcd_item(M, keep, dbeg, dcnt, w) for w in range(grid)]
+    assert sorted(i for i in items if i >= 0) == list(range(W))
+    slow = min(range(8), key=lambda x: speeds[x])
+    assert keep[slow] < M  # the slowest XCD gives work away
+
+
 def test_xcd_plan_equal_speeds_is_the_fixed_split():
     grid, M, keep, dbeg, dcnt = _plan(1, 32, 8, 32768, 128, 8, "contiguous", True)
     assert (grid, M) == (4096, 512)
