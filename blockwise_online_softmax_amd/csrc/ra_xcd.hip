@@ -209,13 +209,13 @@ bool plan_for_shares(const std::vector<float>& wk, int M, const double* tgt, Pla
 }
 
 // The split for per-XCD speeds fin (any positive scale).  The first shares
-// are the whole work times each XCD's share of the speed.  Each round then
+// are the whole work times each XCD's share of the speed.  Each pass then
 // simulates the XCDs' list schedules and scales every share by the mean
 // simulated finish over that XCD's own (an XCD that ends late gets less, one
 // that ends early more).  The plan that ends soonest is kept, if it ends
 // sooner than the fixed split.
 Planned make_plan(const std::vector<float>& wk, int M, const float* fin, int slots) {
-  constexpr int kRounds = 8;
+  constexpr int kPasses = 8;
   double f[kXcds], fs = 0;
   for (int x = 0; x < kXcds; ++x) {
     f[x] = fin[x] > 0.f ? fin[x] : 1.0;
@@ -232,7 +232,7 @@ Planned make_plan(const std::vector<float>& wk, int M, const float* fin, int slo
   for (int x = 0; x < kXcds; ++x) tgt[x] = total * f[x] / fs;
   Planned best = fixed;
   double t_best = t_fixed;
-  for (int round = 0; round < kRounds; ++round) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     Planned pl;
     if (!plan_for_shares(wk, M, tgt, pl)) break;
     const double t = finish(pl, wk, f, slots);
