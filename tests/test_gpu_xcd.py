@@ -39,6 +39,7 @@ def _inputs(B, Hq, Hkv, S, N, D, layout, device, seed):
 CASES = [  # (B, Hq, Hkv, S, N, D, layout, device)
     (1, 16, 4, 8192, 8, 128, "contiguous", -1),
     (1, 16, 4, 8192, 8, 128, "zigzag", -1),
+    (1, 16, 4, 8192, 8, 128, "striped", -1),   # whole striped ring: items tile-major
     (1, 16, 4, 65536, 8, 128, "striped", 5),
     (1, 16, 4, 65536, 8, 128, "zigzag", 3),
     (2, 8, 2, 16384, 8, 64, "contiguous", -1),  # 4-wave kernel, two workgroups per CU
@@ -46,17 +47,25 @@ CASES = [  # (B, Hq, Hkv, S, N, D, layout, device)
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}_D{c[5]}_{c[6]}_S{c[3]}_p{c[7]}")
-def test_split_gives_identical_results(case):
+# one XCD nearly stalled: it gives away almost all of its list
+STALL = [1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0.05]
+
+
+@pytest.mark.parametrize("case,speeds", [(c, SKEW) for c in CASES] + [(CASES[0], STALL)],
+                         ids=lambda c: (f"B{c[0]}_D{c[5]}_{c[6]}_S{c[3]}_p{c[7]}"
+                                        if isinstance(c, tuple) else
+                                        ("stall" if c == STALL else "skew")))
+def test_split_gives_identical_results(case, speeds):
     B, Hq, Hkv, S, N, D, layout, device = case
-    log(f"xcd split {case}")
+    log(f"xcd split {case} speeds {speeds}")
     q, k, v, (qd, kd, vd), pos = _inputs(B, Hq, Hkv, S, N, D, layout, device, 77)
-    grid, M, keep, dbeg, dcnt = ra.ra_xcd_plan(qd, kd, N, layout, True, device, SKEW)
+    grid, M, keep, dbeg, dcnt = ra.ra_xcd_plan(qd, kd, N, layout, True, device, speeds)
     assert grid > 8 * M and sum(dcnt) > 0, "the skewed speeds must give a split launch"
+    log(f"  plan: M {M}, keep {keep}, received {dcnt}")
     try:
         ra.ra_xcd_speeds([1.0] * 8, set=True)  # fixed split
         out0, lse0 = ra.ring_attention(qd, kd, vd, N, layout, True, device)
-        ra.ra_xcd_speeds(SKEW, set=True)
+        ra.ra_xcd_speeds(speeds, set=True)
         out1, lse1 = ra.ring_attention(qd, kd, vd, N, layout, True, device)
         torch.cuda.synchronize()
     finally:
